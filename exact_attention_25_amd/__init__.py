@@ -1,0 +1,19 @@
+"""Exact attention (FlashAttention forward and recompute backward) for MI355X.
+
+The compute lives in ``libfa.so`` (hand-written HIP for gfx950 behind a C
+ABI, declared in ``include/fa.h``).  ``binding`` marshals torch tensors into
+that ABI.  The binding is imported lazily so that ``inputs`` and
+``workloads`` can be used without the library; any use of the compute entry
+points loads ``libfa.so`` and raises if it is missing -- there is no
+fallback implementation.
+"""
+
+_BINDING_NAMES = ("fwd", "bwd", "fa_fwd", "fa_bwd", "bwd_workspace_bytes", "status_str",
+                  "load_library", "FaError", "library_path")
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,276 @@
+"""Float64 CPU oracle for exact attention.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may use this module.  The GPU path never imports it.
+
+Conventions (shared with the C ABI only by *meaning*, not by code):
+
+* Tensors are ``[B, H, N, D]`` arrays (any float dtype; they are upcast to
+  float64 exactly).  ``lse`` is ``[B, H, N]``.
+* ``scale`` multiplies Q K^T before the mask and the softmax, and scales
+  dQ and dK in the backward pass ([FA-CUDA] §1; [FA-WHY] §3.3).
+* ``causal`` masks key j for query i when j > i, i.e. a square, top-left
+  aligned mask with -inf ([FA-CUDA] §1).
+* The log-sum-exp uses the natural logarithm: LSE_i = m_i + ln l_i
+  ([FA-WHY] §3.2, last remark of the section).
+
+Source titles: [FA-CUDA] "CUDA FlashAttention: from online softmax to the
+long-sequence IO limit"; [FA-ALGO] "FlashAttention algorithm details" (ch. 4);
+[FA-WHY] "Why FlashAttention does not need to store the attention matrix";
+[FA-MI50] "FlashAttention dataflow and engineering validation on MI50".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _check4(*arrays):
+    for a in arrays:
+        if a.ndim != 4:
+            raise ValueError("expected [B, H, N, D] arrays, got shape %r" % (a.shape,))
+
+
+# ---------------------------------------------------------------------------
+# Plain definition: two-pass safe softmax over complete, materialised rows.
+# ---------------------------------------------------------------------------
+def _scores_block(qh, kh, i0, i1, causal, scale):
+    """Rows i0..i1-1 of S = scale * Q K^T with the causal -inf mask applied.
+
+    With ``causal`` the rows only ever see keys 0..i1-1, so the block is
+    truncated there; the truncated columns would all be -inf anyway.
+    Definition: [FA-CUDA] §1 (S = QK^T/sqrt(D) + M, M_ij = -inf for j > i).
+    """
+    nk = i1 if causal else kh.shape[0]
+    s = scale * (qh[i0:i1] @ kh[:nk].T)
+    if causal:
+        rows = np.arange(i0, i1)[:, None]
+        cols = np.arange(nk)[None, :]
+        s = np.where(cols > rows, NEG_INF, s)
+    return s, nk
+
+
+def _safe_softmax_rows(s):
+    """Safe softmax of complete rows: subtract the row max, exponentiate,
+    normalise ([FA-WHY] §3.1).  Returns (P, m, l) with l = sum exp(s - m)."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def attention_forward(q, k, v, causal, scale, row_block=256):
+    """O = softmax(scale * Q K^T + M) V and LSE, by the plain definition.
+
+    For every (b, h) and every block of ``row_block`` query rows the complete
+    score rows are materialised in float64, softmax is taken with the
+    two-pass safe formula and O = P V.  LSE_i = m_i + ln(sum_j exp(S_ij - m_i)).
+    Sources: [FA-CUDA] §1 (definition), [FA-WHY] §3.1 (safe softmax) and
+    §3.2 (LSE = m + log l).
+
+    Returns (O, LSE) as float64 arrays of shape [B,H,N,D] and [B,H,N].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check4(q, k, v)
+    B, H, N, D = q.shape
+    o = np.empty((B, H, N, D))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = q[b, h], k[b, h], v[b, h]
+            for i0 in range(0, N, row_block):
+                i1 = min(N, i0 + row_block)
+                s, nk = _scores_block(qh, kh, i0, i1, causal, scale)
+                p, m, l = _safe_softmax_rows(s)
+                o[b, h, i0:i1] = p @ vh[:nk]
+                lse[b, h, i0:i1] = m + np.log(l)
+    return o, lse
+
+
+def attention_probs(q, k, causal, scale):
+    """The full probability matrix P for one head (q, k: [N, D]).
+
+    For small inputs only (it is N x N).  Same definition as above.
+    """
+    q, k = _f64(q), _f64(k)
+    n = q.shape[0]
+    s, _ = _scores_block(q, k, 0, n, False, scale)
+    if causal:
+        s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], NEG_INF, s)
+    p, _, _ = _safe_softmax_rows(s)
+    return p
+
+
+def attention_backward(q, k, v, do, causal, scale, row_block=256):
+    """dQ, dK, dV of L with dL/dO = ``do``, by the plain definition.
+
+    With P the forward probabilities and G = dO:
+        dP = G V^T,  Delta_i = sum_j P_ij dP_ij,  dS = P * (dP - Delta),
+        dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T G.
+    [FA-WHY] §3.3 states these formulas including the scale factor;
+    [FA-ALGO] §4.3.1 gives the same ones with the scale omitted.  P is
+    materialised in float64 a block of query rows at a time; sums over
+    query rows are split over those blocks.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    _check4(q, k, v, do)
+    B, H, N, D = q.shape
+    dq = np.zeros((B, H, N, D))
+    dk = np.zeros((B, H, N, D))
+    dv = np.zeros((B, H, N, D))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, gh = q[b, h], k[b, h], v[b, h], do[b, h]
+            for i0 in range(0, N, row_block):
+                i1 = min(N, i0 + row_block)
+                s, nk = _scores_block(qh, kh, i0, i1, causal, scale)
+                p, _, _ = _safe_softmax_rows(s)
+                g = gh[i0:i1]
+                dv[b, h, :nk] += p.T @ g
+                dp = g @ vh[:nk].T
+                delta = (p * dp).sum(axis=1)
+                ds = p * (dp - delta[:, None])
+                dq[b, h, i0:i1] = scale * (ds @ kh[:nk])
+                dk[b, h, :nk] += scale * (ds.T @ qh[i0:i1])
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Online (streaming) recurrence, written separately from the definition above.
+# ---------------------------------------------------------------------------
+def merge_states(m_a, l_a, o_a, m_b, l_b, o_b):
+    """Merge two partial softmax states of the same query rows.
+
+    A state (m, l, o) holds the running max m, l = sum exp(s - m) and the
+    unnormalised o = sum exp(s - m) v over the keys it has seen.  The merged
+    state takes m = max(m_a, m_b) and rescales each side by exp(m_side - m)
+    ([FA-CUDA] §4, alpha and beta).  A side with m = -inf has seen no
+    visible key and contributes zero (the guard of [FA-CUDA] §6 and
+    [FA-WHY] §3.2: its rescale factor is taken as 0, never exp(-inf+inf)).
+
+    Arrays: m_*, l_* shape [R]; o_* shape [R, D] (or None to skip o).
+    """
+    m_a, l_a, m_b, l_b = _f64(m_a), _f64(l_a), _f64(m_b), _f64(l_b)
+    m = np.maximum(m_a, m_b)
+    fin = np.isfinite(m)
+    m_safe = np.where(fin, m, 0.0)
+    alpha = np.where(np.isneginf(m_a), 0.0, np.exp(np.where(np.isneginf(m_a), 0.0, m_a) - m_safe))
+    beta = np.where(np.isneginf(m_b), 0.0, np.exp(np.where(np.isneginf(m_b), 0.0, m_b) - m_safe))
+    l = alpha * l_a + beta * l_b
+    if o_a is None:
+        return m, l, None
+    o = alpha[:, None] * _f64(o_a) + beta[:, None] * _f64(o_b)
+    return m, l, o
+
+
+def online_forward(q, k, v, causal, scale, block_q=64, block_k=64,
+                   ablate_rescale=False, trace_row=None):
+    """Tiled attention with the online softmax recurrence, one head.
+
+    q, k, v: [N, D].  The outer loop walks query tiles of ``block_q`` rows,
+    the inner loop key/value tiles of ``block_k`` keys ([FA-ALGO] §4.2.1;
+    [FA-CUDA] §5.1).  Per tile ([FA-WHY] §3.2; [FA-ALGO] §4.2.1 steps 1-5):
+
+        S    = scale * Q_i K_j^T, causal entries j > i set to -inf first
+        m'   = max(m, rowmax S)
+        corr = exp(m - m')           (0 when m is still -inf)
+        l    = corr * l + rowsum exp(S - m')
+        O    = corr * O + exp(S - m') V_j
+        m    = m'
+
+    and finally O / l and LSE = m + ln l.  Key tiles that lie wholly above
+    the diagonal are skipped ([FA-WHY] §4.5).
+
+    ``ablate_rescale=True`` replaces corr by 1, reproducing the broken
+    variant of [FA-WHY] §09; it exists only so a test can show the pin
+    catches that mistake.  ``trace_row`` (an int) records, for that query
+    row, (key tile start, m, l, corr) after every key tile it visits.
+
+    Returns (O [N,D], LSE [N], info) where info holds ``tiles`` (number of
+    (query tile, key tile) pairs computed) and ``trace`` (list or None).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, d = q.shape
+    o_out = np.empty((n, d))
+    lse_out = np.empty(n)
+    tiles = 0
+    trace = [] if trace_row is not None else None
+    for i0 in range(0, n, block_q):
+        i1 = min(n, i0 + block_q)
+        m = np.full(i1 - i0, NEG_INF)
+        l = np.zeros(i1 - i0)
+        acc = np.zeros((i1 - i0, d))
+        for j0 in range(0, n, block_k):
+            j1 = min(n, j0 + block_k)
+            if causal and j0 > i1 - 1:
+                break  # every later key tile is above the diagonal too
+            tiles += 1
+            s = scale * (q[i0:i1] @ k[j0:j1].T)
+            if causal:
+                rows = np.arange(i0, i1)[:, None]
+                cols = np.arange(j0, j1)[None, :]
+                s = np.where(cols > rows, NEG_INF, s)
+            m_new = np.maximum(m, s.max(axis=1))
+            m_ref = np.where(np.isneginf(m_new), 0.0, m_new)
+            if ablate_rescale:
+                corr = np.ones_like(m)
+            else:
+                corr = np.where(np.isneginf(m), 0.0, np.exp(np.where(np.isneginf(m), 0.0, m) - m_ref))
+            p = np.exp(s - m_ref[:, None])
+            l = corr * l + p.sum(axis=1)
+            acc = corr[:, None] * acc + p @ v[j0:j1]
+            m = m_new
+            if trace is not None and i0 <= trace_row < i1:
+                r = trace_row - i0
+                trace.append((j0, float(m[r]), float(l[r]), float(corr[r])))
+        o_out[i0:i1] = acc / l[:, None]
+        lse_out[i0:i1] = m + np.log(l)
+    return o_out, lse_out, {"tiles": tiles, "trace": trace}
+
+
+def causal_tile_count(n, block):
+    """Number of (query tile, key tile) pairs a causal tiled pass computes
+    when tiles wholly above the diagonal are skipped ([FA-WHY] §4.5),
+    counted by enumeration."""
+    t = -(-n // block)
+    count = 0
+    for i in range(t):
+        for j in range(t):
+            if j * block <= i * block + block - 1:
+                count += 1
+    return count
+
+
+# ---------------------------------------------------------------------------
+# Pure-Python brute force for tiny inputs.
+# ---------------------------------------------------------------------------
+def brute_force_forward(q, k, v, causal, scale):
+    """Attention of one head with Python floats, math.exp and math.fsum.
+
+    q, k, v: nested sequences [N][D] (N <= 8 expected).  Direct transcription
+    of the definition ([FA-CUDA] §1, safe softmax per [FA-WHY] §3.1), no
+    numpy.  Returns (O as list of lists, LSE as list).
+    """
+    n = len(q)
+    d = len(q[0])
+    out, lse = [], []
+    for i in range(n):
+        keys = range(i + 1) if causal else range(n)
+        s = [scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        tot = math.fsum(e)
+        row = []
+        for t in range(d):
+            row.append(math.fsum(e[idx] * v[j][t] for idx, j in enumerate(keys)) / tot)
+        out.append(row)
+        lse.append(m + math.log(tot))
+    return out, lse

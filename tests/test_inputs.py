@@ -1,0 +1,40 @@
+"""The seeded input generator (no GPU): determinism, rounding, head sampling."""
+
+import numpy as np
+import torch
+
+from exact_attention_25_amd.inputs import make_inputs, round_bf16, round_fp16
+
+
+def test_rounding_matches_torch_casts():
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 37
+    x[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -11, 65504.0]  # ties
+    t = torch.from_numpy(x)
+    assert np.array_equal(round_bf16(x), t.to(torch.bfloat16).to(torch.float32).numpy())
+    assert np.array_equal(round_fp16(x), t.to(torch.float16).to(torch.float32).numpy())
+
+
+def test_values_exact_in_storage_type():
+    for dt, tdt in (("fp16", torch.float16), ("bf16", torch.bfloat16)):
+        d = make_inputs(1, 2, 64, 16, dt, seed=3, spiky_keys=True, with_dout=True)
+        for a in d.values():
+            t = torch.from_numpy(a)
+            assert torch.equal(t.to(tdt).to(torch.float32), t)
+
+
+def test_head_sampling_reproduces_full_draw():
+    full = make_inputs(2, 3, 32, 8, "bf16", seed=7, spiky_keys=True, with_dout=True)
+    heads = [(0, 2), (1, 0)]
+    part = make_inputs(2, 3, 32, 8, "bf16", seed=7, spiky_keys=True, with_dout=True, heads=heads)
+    for name in full:
+        for i, (b, h) in enumerate(heads):
+            assert np.array_equal(full[name][b, h], part[name][i])
+
+
+def test_spiky_rows():
+    a = make_inputs(1, 1, 256, 8, "bf16", seed=4, spiky_keys=False)
+    b = make_inputs(1, 1, 256, 8, "bf16", seed=4, spiky_keys=True)
+    rows = np.arange(256)
+    assert np.array_equal(b["k"][0, 0, rows % 64 == 0], 8 * a["k"][0, 0, rows % 64 == 0])
+    assert np.array_equal(b["k"][0, 0, rows % 64 != 0], a["k"][0, 0, rows % 64 != 0])
+    assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["v"], b["v"])

@@ -1,0 +1,298 @@
+"""Pins for the float64 CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: numbers the pages
+print (fixtures under tests/golden, each with its citation), closed forms,
+invariants of the mathematics, finite differences and a pure-Python brute
+force.  A dropped term, a wrong sign or index, or a transposed operand in
+oracle/attention.py fails at least one of these.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (
+    attention_backward,
+    attention_forward,
+    attention_probs,
+    brute_force_forward,
+    causal_tile_count,
+    merge_states,
+    online_forward,
+)
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _heads(x):
+    return x[None, None]
+
+
+# --------------------------------------------------------------------------
+# Worked example of the MI50 notes, section 2.2
+# --------------------------------------------------------------------------
+def test_worked_row_block_merge(golden_dir):
+    g = _load(golden_dir, "worked_row_mi50.json")
+    (a, b) = g["blocks"]
+    # each block's own state: its max and sum exp(s - max)
+    m_a, l_a = max(a), sum(math.exp(x - max(a)) for x in a)
+    m_b, l_b = max(b), sum(math.exp(x - max(b)) for x in b)
+    assert m_a == g["block1_max"] and m_b == g["block2_max"]
+    nd = g["printed_decimals"]
+    assert round(l_a, nd) == g["block1_sum_printed"]
+    assert round(l_b, nd) == g["block2_sum_printed"]
+    assert round(math.exp(m_a - m_b), nd) == g["rescale_printed"]
+    m, l, _ = merge_states([m_a], [l_a], None, [m_b], [l_b], None)
+    closed = 1.0 + math.exp(-1) + math.exp(-2) + math.exp(-3)
+    assert m[0] == 4.0
+    assert abs(l[0] - closed) < 1e-15
+    assert round(l[0], nd) == g["merged_sum_printed"]
+
+
+def test_worked_row_through_forward(golden_dir):
+    g = _load(golden_dir, "worked_row_mi50.json")
+    row = np.array(g["row"])
+    # one query, D=1, q=1 and k_j = s_j gives the score row exactly (scale 1)
+    q = np.ones((1, 1))
+    k = row[:, None]
+    v = np.eye(4)[:, :1] * 0 + np.arange(4.0)[:, None]  # v_j = j
+    closed_l = 1.0 + math.exp(-1) + math.exp(-2) + math.exp(-3)
+    qq = np.zeros((4, 1)); qq[:1] = q  # 4 queries so shapes are square
+    o, lse = attention_forward(_heads(qq), _heads(k), _heads(v), False, 1.0)
+    assert abs(lse[0, 0, 0] - (4.0 + math.log(closed_l))) < 1e-14
+    p = np.exp(row - 4.0) / closed_l
+    assert abs(o[0, 0, 0, 0] - float(p @ np.arange(4.0))) < 1e-14
+    # the online pass with key tiles [1,2] | [3,4] reaches the same state
+    _, lse_on, info = online_forward(qq, k, v, False, 1.0, block_q=4, block_k=2, trace_row=0)
+    (j0, m1, l1, c1), (j1, m2, l2, c2) = info["trace"]
+    assert (m1, m2) == (2.0, 4.0)
+    assert abs(l1 - (math.exp(-1) + 1)) < 1e-15
+    assert abs(c2 - math.exp(-2)) < 1e-15
+    assert abs(l2 - closed_l) < 1e-15
+    assert abs(lse_on[0] - lse[0, 0, 0]) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# "Why FlashAttention ..." section 4.1 trace, 4.2 table, 4.5 count, 09 ablation
+# --------------------------------------------------------------------------
+def _page_qkv(seed, n, d):
+    rng = np.random.default_rng(seed)
+    q = rng.normal(size=(n, d))
+    k = rng.normal(size=(n, d))
+    v = rng.normal(size=(n, d))
+    return q, k, v
+
+
+def test_recurrence_trace_matches_page(golden_dir):
+    g = _load(golden_dir, "recurrence_trace_why.json")
+    q, k, v = _page_qkv(g["seed"], g["N"], g["D"])
+    _, _, info = online_forward(q, k, v, False, 1.0 / math.sqrt(g["D"]),
+                                block_q=g["N"], block_k=g["block_k"], trace_row=0)
+    tol = 0.5 * 10.0 ** (-g["printed_decimals"]) + 1e-12
+    assert len(info["trace"]) == len(g["rows"])
+    for (j0, m, l, corr), row in zip(info["trace"], g["rows"]):
+        assert j0 == row["j"]
+        assert abs(m - row["m"]) <= tol
+        assert abs(l - row["l"]) <= tol
+        assert abs(corr - row["corr"]) <= tol
+
+
+@pytest.mark.parametrize("n", [256, 1024])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_equals_definition_float64(golden_dir, n, causal):
+    g = _load(golden_dir, "exactness_table_why.json")
+    q, k, v = _page_qkv(n, n, 64)
+    scale = 1.0 / 8.0
+    ref, lse_ref = attention_forward(_heads(q), _heads(k), _heads(v), causal, scale)
+    got, lse, _ = online_forward(q, k, v, causal, scale, block_q=64, block_k=64)
+    err = np.abs(ref[0, 0] - got).max()
+    page = max(r["max_abs"] for r in g["rows"])
+    # rounding level: the page's table tops out below 1e-15
+    assert err <= 10 * page
+    assert np.abs(lse_ref[0, 0] - lse).max() <= 1e-13
+
+
+def test_rescale_ablation_matches_page(golden_dir):
+    g = _load(golden_dir, "rescale_ablation_why.json")
+    q, k, v = _page_qkv(g["seed"], g["N"], g["D"])
+    scale = 1.0 / math.sqrt(g["D"])
+    ref, _ = attention_forward(_heads(q), _heads(k), _heads(v), False, scale)
+    bad, _, _ = online_forward(q, k, v, False, scale, ablate_rescale=True)
+    diff = np.abs(ref[0, 0] - bad)
+    assert round(float(diff.max()), 3) == g["max_abs_printed"]
+    assert round(float(diff.mean()), 4) == g["mean_abs_printed"]
+    good, _, _ = online_forward(q, k, v, False, scale)
+    assert np.abs(ref[0, 0] - good).max() < 1e-14
+
+
+def test_causal_tile_count(golden_dir):
+    g = _load(golden_dir, "causal_tiles_why.json")
+    t = g["N"] // g["block"]
+    assert t * t == g["tiles_noncausal"]
+    cnt = causal_tile_count(g["N"], g["block"])
+    assert cnt == g["tiles_causal"] == t * (t + 1) // 2
+    assert round(100.0 * (1 - cnt / (t * t)), 1) == g["skipped_percent_printed"]
+    # the online pass visits exactly that many tiles
+    q, k, v = (np.ones((g["N"], 2)),) * 3
+    _, _, info = online_forward(q, k, v, True, 1.0, block_q=g["block"], block_k=g["block"])
+    assert info["tiles"] == cnt
+
+
+# --------------------------------------------------------------------------
+# Closed forms and special cases
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    q, k = _rand(3, 33, 16), _rand(4, 33, 16)
+    p = attention_probs(q, k, causal, 0.25)
+    assert np.abs(p.sum(axis=1) - 1.0).max() < 1e-14
+    if causal:
+        assert np.all(p[np.triu_indices(33, 1)] == 0.0)
+
+
+def test_causal_row_zero_is_first_value():
+    q, k, v = _rand(5, 1, 1, 17, 8), _rand(6, 1, 1, 17, 8), _rand(7, 1, 1, 17, 8)
+    o, lse = attention_forward(q, k, v, True, 0.3)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0])
+    assert lse[0, 0, 0] == 0.3 * float(q[0, 0, 0] @ k[0, 0, 0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_keys_give_prefix_mean(causal):
+    n, d = 19, 6
+    q = _rand(8, 1, 1, n, d)
+    k = np.tile(_rand(9, d), (1, 1, n, 1))
+    v = _rand(10, 1, 1, n, d)
+    o, lse = attention_forward(q, k, v, causal, 0.7)
+    for i in range(n):
+        cnt = i + 1 if causal else n
+        assert np.abs(o[0, 0, i] - v[0, 0, :cnt].mean(axis=0)).max() < 1e-14
+        s = 0.7 * float(q[0, 0, i] @ k[0, 0, 0])
+        assert abs(lse[0, 0, i] - (s + math.log(cnt))) < 1e-13
+
+
+def test_largest_fp16_inputs_scale_one():
+    # the page on MI50 tuning stresses every input equal to 65504 with scale 1
+    x = np.full((1, 2, 9, 4), 65504.0)
+    o, lse = attention_forward(x, x, x, True, 1.0)
+    assert np.abs(o - 65504.0).max() <= 65504.0 * 4e-16 * 9
+    s = 65504.0 * 65504.0 * 4
+    for i in range(9):
+        assert lse[0, 0, i] == s + math.log(i + 1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    q, k, v = _rand(11, 1, 2, 23, 8), _rand(12, 1, 2, 23, 8), _rand(13, 1, 2, 23, 8)
+    do = _rand(14, 1, 2, 23, 8)
+    u = _rand(15, 8)
+    scale = 0.4
+    o1, l1 = attention_forward(q, k, v, causal, scale)
+    o2, l2 = attention_forward(q, k + u, v, causal, scale)
+    assert np.abs(o1 - o2).max() < 1e-13
+    assert np.abs((l2 - l1) - scale * (q @ u)).max() < 1e-12
+    g1 = attention_backward(q, k, v, do, causal, scale)
+    g2 = attention_backward(q, k + u, v, do, causal, scale)
+    for a, b in zip(g1, g2):
+        assert np.abs(a - b).max() < 1e-12
+
+
+def test_joint_key_value_permutation_invariance():
+    q, k, v = _rand(16, 1, 1, 29, 8), _rand(17, 1, 1, 29, 8), _rand(18, 1, 1, 29, 8)
+    perm = np.random.default_rng(19).permutation(29)
+    o1, l1 = attention_forward(q, k, v, False, 0.5)
+    o2, l2 = attention_forward(q, k[:, :, perm], v[:, :, perm], False, 0.5)
+    assert np.abs(o1 - o2).max() < 1e-14 and np.abs(l1 - l2).max() < 1e-13
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 8])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_agrees(n, causal):
+    d = 4
+    q, k, v = _rand(20 + n, n, d), _rand(30 + n, n, d), _rand(40 + n, n, d)
+    scale = 1.0 / math.sqrt(d)
+    ob, lb = brute_force_forward(q.tolist(), k.tolist(), v.tolist(), causal, scale)
+    o, lse = attention_forward(_heads(q), _heads(k), _heads(v), causal, scale)
+    on, lon, _ = online_forward(q, k, v, causal, scale, block_q=3, block_k=2)
+    assert np.abs(o[0, 0] - np.array(ob)).max() < 1e-14
+    assert np.abs(lse[0, 0] - np.array(lb)).max() < 1e-14
+    assert np.abs(on - np.array(ob)).max() < 1e-14
+    assert np.abs(lon - np.array(lb)).max() < 1e-14
+
+
+def test_row_block_split_does_not_change_result():
+    q, k, v = _rand(50, 1, 1, 70, 8), _rand(51, 1, 1, 70, 8), _rand(52, 1, 1, 70, 8)
+    for causal in (False, True):
+        a = attention_forward(q, k, v, causal, 0.3, row_block=256)
+        b = attention_forward(q, k, v, causal, 0.3, row_block=7)
+        assert np.abs(a[0] - b[0]).max() < 1e-15
+
+
+def test_merge_guard_for_empty_side():
+    # a side that has seen no visible key (m = -inf) contributes nothing
+    m, l, o = merge_states([-np.inf], [0.0], [[0.0, 0.0]], [1.5], [2.0], [[3.0, 4.0]])
+    assert m[0] == 1.5 and l[0] == 2.0 and np.array_equal(o[0], [3.0, 4.0])
+    assert not np.any(np.isnan(o))
+
+
+# --------------------------------------------------------------------------
+# Backward
+# --------------------------------------------------------------------------
+def _loss(q, k, v, do, causal, scale):
+    o, _ = attention_forward(q, k, v, causal, scale)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences(causal):
+    n, d = 7, 4
+    q, k, v = _rand(60, 1, 1, n, d), _rand(61, 1, 1, n, d), _rand(62, 1, 1, n, d)
+    do = _rand(63, 1, 1, n, d)
+    scale = 0.6
+    grads = attention_backward(q, k, v, do, causal, scale)
+    h = 1e-6
+    for gi, name in enumerate("qkv"):
+        base = [q, k, v]
+        num = np.zeros_like(base[gi])
+        for idx in np.ndindex(base[gi].shape):
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[gi][idx] += h
+            minus[gi][idx] -= h
+            num[idx] = (_loss(*plus, do, causal, scale) - _loss(*minus, do, causal, scale)) / (2 * h)
+        assert np.abs(num - grads[gi]).max() < 1e-8, name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    n, d = 40, 8
+    q, k, v = _rand(70, 1, 2, n, d), _rand(71, 1, 2, n, d), _rand(72, 1, 2, n, d)
+    do = _rand(73, 1, 2, n, d)
+    dq, dk, dv = attention_backward(q, k, v, do, causal, 0.35, row_block=16)
+    # softmax rows sum to one, so dS rows sum to zero and sum_j dK_j = 0
+    assert np.abs(dk.sum(axis=2)).max() < 1e-12
+    # dV = P^T dO and P's rows sum to one
+    assert np.abs(dv.sum(axis=2) - do.sum(axis=2)).max() < 1e-12
+    # Delta_i = rowsum(P * dP) equals rowsum(dO * O) because O = P V
+    o, _ = attention_forward(q, k, v, causal, 0.35)
+    p = attention_probs(q[0, 0], k[0, 0], causal, 0.35)
+    dp = do[0, 0] @ v[0, 0].T
+    assert np.abs((p * dp).sum(axis=1) - (do[0, 0] * o[0, 0]).sum(axis=1)).max() < 1e-12
+
+
+def test_constant_keys_give_zero_dq():
+    n, d = 12, 4
+    q, v, do = _rand(80, 1, 1, n, d), _rand(81, 1, 1, n, d), _rand(82, 1, 1, n, d)
+    k = np.tile(_rand(83, d), (1, 1, n, 1))
+    dq, _, _ = attention_backward(q, k, v, do, True, 0.5)
+    assert np.abs(dq).max() < 1e-13
