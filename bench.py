@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--mode bench|copy|fwd-only|bwd-only]
+
+Default workload: causal fp16 attention forward, B=1 H=32 N=8192 D=128 (the
+headline metric: causal forward TFLOP/s and its fraction of the dense fp16
+MFMA peak).  A timed step is one fa_fwd call over the whole batch; inputs are
+seeded synthetic tensors already resident in HBM.  The same run also times
+the backward (fa_bwd on the same shapes) and reports it under "bwd".
+
+Prints ONE JSON line.  Timing uses torch.cuda events on the stream the
+library launches on (torch's current stream).  The cpu_baseline leg times
+the float64 CPU oracle on a bounded sample of the same workload.
+
+--mode copy runs only a plain device copy of known size; it exists so that
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters can be calibrated against a
+kernel whose HBM traffic is known.
+--mode fwd-only / bwd-only launch just that pass K times (for profiling).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd TFLOP/s + % MFMA peak, B1 H32 D128 N=8192 fp16"
+PEAK_TFLOPS_FP16 = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# The pages' own figure for exactly this workload (causal fp16, B1 H32 D128,
+# N=8192): 25.854 ms on an RTX 3060 Laptop GPU with PyTorch's FlashAttention
+# backend ("CUDA FlashAttention: from online softmax to the long-sequence IO
+# limit", §8) = 2*1*32*8192^2*128 FLOP / 25.854 ms = 21.26 TFLOP/s.
+PAGE_BASELINE_TFLOPS = 2 * 32 * 8192 ** 2 * 128 / 25.854e-3 / 1e12
+
+FWD_SOURCES = ["exact_attention_25_amd/csrc/fa_fwd.hip", "exact_attention_25_amd/csrc/fa_common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_causal_b1h32n8192d128_fp16_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--mode", default="bench", choices=["bench", "copy", "fwd-only", "bwd-only"])
+    return p.parse_args()
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name, launches_per_step=1):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    on the current forward-kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("workload") != workload_name or t.get("source_hash") != source_hash(FWD_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """Time the float64 oracle on whole heads of the workload until about
+    `seconds` have passed; report algorithmic TFLOP/s on that sample."""
+    import numpy as np
+    from exact_attention_25_amd.inputs import make_inputs
+    from oracle import attention_forward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    heads_done, t_total = 0, 0.0
+    per_head = w.fwd_flops() / (w.B * w.H)
+    order = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in order:
+        inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys, heads=[(b, h)])
+        q, k, v = (inp[n][None] for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        attention_forward(q, k, v, w.causal, w.scale)
+        t_total += time.perf_counter() - t0
+        heads_done += 1
+        if t_total >= seconds:
+            break
+    return {
+        "value": heads_done * per_head / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d heads of %s, float64 numpy, %.1f s" % (heads_done, len(order), w.name, t_total),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested; run with --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_25_amd as fa
+    from exact_attention_25_amd import workloads
+    from exact_attention_25_amd.inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.mode == "copy":
+        n = 1 << 30
+        src = torch.ones(n // 2, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "launches": args.warmup + args.steps}), flush=True)
+        return
+
+    w = workloads.HEADLINE
+    if args.workload:
+        named = {x.name: x for x in workloads.ALL}
+        if args.workload not in named:
+            sys.exit("unknown workload %s; choose from %s" % (args.workload, ", ".join(named)))
+        w = named[args.workload]
+
+    tdt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+    inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys, with_dout=True)
+    q, k, v, do = (torch.from_numpy(inp[n]).to(dev).to(tdt).contiguous() for n in ("q", "k", "v", "do"))
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run_fwd():
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    ws = torch.empty(max(256, fa.bwd_workspace_bytes(w.B, w.H, w.N, w.D, w.causal, 0 if w.dtype == "fp16" else 1)),
+                     dtype=torch.uint8, device=dev)
+
+    def run_bwd():
+        return fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
+
+    if args.mode in ("fwd-only", "bwd-only"):
+        run_fwd()
+        fn = run_fwd if args.mode == "fwd-only" else run_bwd
+        for _ in range(args.warmup + args.steps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": args.mode, "workload": w.name, "launches": args.warmup + args.steps}), flush=True)
+        return
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per call
+
+    ms = timed(run_fwd, args.steps, args.warmup)
+    tflops = w.fwd_flops() / (ms * 1e-3) / 1e12
+    bwd_ms = timed(run_bwd, max(1, args.steps // 2), max(1, args.warmup // 2))
+    bwd_tflops = w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
+
+    traffic = load_traffic(w.name)
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / PAGE_BASELINE_TFLOPS, 2) if w is workloads.HEADLINE else None,
+        "vs_baseline_ref": "RTX 3060 Laptop, PyTorch FlashAttention backend, 25.854 ms = 21.26 TFLOP/s "
+                           "(another machine: context only)" if w is workloads.HEADLINE else None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) rounded to %s (seed %d)" % (w.dtype, w.seed),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "causal": w.causal,
+                   "scale": w.scale},
+        "pct_mfma_peak": round(100 * tflops / PEAK_TFLOPS_FP16, 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "fwd_kernel<%d,%s>" % (w.D, "causal" if w.causal else "full"),
+            "achieved": round(tflops, 2),
+            "peak": PEAK_TFLOPS_FP16,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_TFLOPS_FP16, 4),
+            "traffic": traffic,
+        },
+        "hbm_compulsory_gbs": round(w.io_bytes_fwd() / (ms * 1e-3) / 1e9, 1),
+        "bwd": {
+            "ms_per_call": round(bwd_ms, 4),
+            "tflops": round(bwd_tflops, 2),
+            "frac_mfma_peak": round(bwd_tflops / PEAK_TFLOPS_FP16, 4),
+            "flops_counted": "10*B*H*N^2*D (causal: half): five N x N x D products",
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+"""Thin ctypes binding of libfa.so (declared in include/fa.h).
+
+Argument marshalling only: tensors are checked, outputs allocated with torch
+(device memory is torch's), and the C entry points are called on the current
+torch stream.  Every step of the attention computation runs in the library's
+HIP kernels.  If libfa.so is missing this module raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from .build_lib import LIB_PATH
+
+FA_OK = 0
+FA_FP16 = 0
+FA_BF16 = 1
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__("%s%s" % (what + ": " if what else "", status_str(status)))
+
+
+_lib = None
+
+
+def library_path():
+    return os.environ.get("FA_LIBRARY", LIB_PATH)
+
+
+def load_library():
+    """Load libfa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError("libfa.so is not built (%s); run __graft_entry__.build() or "
+                          "python -m exact_attention_25_amd.build_lib" % path)
+    lib = ctypes.CDLL(path)
+    lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                           ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                           ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(status):
+    return load_library().fa_status_str(int(status)).decode()
+
+
+# ---- raw entry points: plain integers as pointers, same names as the C ABI ----
+def fa_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, stream):
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, N, D, int(causal), float(scale), int(dtype), stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype,
+           workspace, workspace_bytes, stream):
+    return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, int(causal),
+                                 float(scale), int(dtype), workspace, workspace_bytes, stream)
+
+
+def bwd_workspace_bytes(B, H, N, D, causal, dtype):
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, D, int(causal), int(dtype)))
+
+
+# ---- torch-tensor convenience wrappers ----
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return FA_FP16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError("attention tensors must be float16 or bfloat16, got %s" % t.dtype)
+
+
+def _check(tensors, shape, dtype, device):
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if t.device != device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        if t.dtype != dtype:
+            raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous [B, H, N, D]" % name)
+
+
+def _stream_handle(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """O, LSE = attention forward of [B, H, N, D] fp16/bf16 device tensors.
+
+    Returns (o, lse) with o like q and lse float32 [B, H, N].
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, D]")
+    B, H, N, D = q.shape
+    _check({"q": q, "k": k, "v": v}, q.shape, q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check({"out": out}, q.shape, q.dtype, q.device)
+    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, N, D, causal, scale, _dtype_code(q), _stream_handle(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
+    """dQ, dK, dV of the attention forward, by recomputation."""
+    import torch
+    B, H, N, D = q.shape
+    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
+    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code = _dtype_code(q)
+    need = bwd_workspace_bytes(B, H, N, D, causal, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, causal, scale, code,
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

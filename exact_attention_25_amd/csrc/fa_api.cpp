@@ -1,0 +1,108 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument checks, then
+// dispatch to the template instance for (D, causal, dtype) on the caller's
+// stream.  Every check runs before anything is enqueued, so a rejected call
+// leaves the stream untouched.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxWorkgroups = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_FP16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (N % 64 != 0) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_UNSUPPORTED;
+  // Grid sizes: B*H*ceil(N/64) workgroups at most; B*H must fit an int.
+  if (B > kMaxWorkgroups / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  if (bh > kMaxWorkgroups / (N / 64)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N is not positive, or the problem is too large";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: need D in {64,128}, dtype fp16/bf16, causal 0/1, N % 64 == 0, finite scale > 0";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+           int64_t N, int64_t D, int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.N = N;
+  a.BH = static_cast<int>(B * H);
+  const int bm = fa::fwd_block_m();
+  a.n_qtiles = static_cast<int>((N + bm - 1) / bm);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_fwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype) {
+  if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK) return 0;
+  const size_t bytes = static_cast<size_t>(B * H * N) * sizeof(float);
+  return (bytes + 255) & ~static_cast<size_t>(255);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
+           int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, D, causal, dtype);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = static_cast<float*>(workspace);
+  a.N = N;
+  a.BH = static_cast<int>(B * H);
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_bwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// fa_common.hpp -- device helpers shared by the forward and backward kernels.
+//
+// gfx950 (CDNA4) facts these helpers rely on:
+//  * A wavefront has 64 lanes.
+//  * v_mfma_f32_32x32x16_{f16,bf16}: D(32x32,f32) = A(32x16) * B(16x32) + C.
+//    A lane l supplies 8 consecutive K-slots of row (l % 32) of A, and the
+//    same 8 K-slots of column (l % 32) of B; lanes 0-31 and 32-63 cover the
+//    two halves of K.  Because A and B use the same slot order, any
+//    consistent assignment of real indices to (lane half, element) pairs
+//    gives the right contraction.
+//  * The 16 accumulator registers of lane l hold column n = l % 32 and rows
+//    m = 8*(r/4) + 4*(l/32) + (r%4), r = 0..15.
+//  * LDS has 64 banks of 4 bytes.  Tiles are stored as 16-byte chunks with
+//    an XOR swizzle inside every 256-byte line (see swz()), so that 16 lanes
+//    reading the same chunk column of 16 different rows hit 16 different
+//    chunk positions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Fp16 {
+  static constexpr int id = 0;
+};
+struct Bf16 {
+  static constexpr int id = 1;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <class T>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<Fp16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<Bf16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> one dword of two 16-bit values (lo = a), round to nearest even.
+template <class T>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+
+template <>
+__device__ __forceinline__ uint32_t pack2<Fp16>(float a, float b) {
+  _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+template <>
+__device__ __forceinline__ uint32_t pack2<Bf16>(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Eight floats (elements lo..lo+7 of an accumulator) -> one MFMA operand.
+template <class T>
+__device__ __forceinline__ u32x4 pack8(const f32x16& s, int lo) {
+  u32x4 r;
+  r[0] = pack2<T>(s[lo + 0], s[lo + 1]);
+  r[1] = pack2<T>(s[lo + 2], s[lo + 3]);
+  r[2] = pack2<T>(s[lo + 4], s[lo + 5]);
+  r[3] = pack2<T>(s[lo + 6], s[lo + 7]);
+  return r;
+}
+
+// 16-byte-chunk swizzle: within each 256-byte line (16 chunks) the chunk
+// position is XORed with the line index.
+__device__ __forceinline__ int swz(int chunk) { return chunk ^ ((chunk >> 4) & 15); }
+
+// Swap bits 2 and 3 of a row index inside a 32-row MFMA block.  Reading
+// operand rows in this order makes accumulator register r of lane-half g
+// hold row 16*(r/8) + 8*g + (r%8) -- eight consecutive rows per half -- so a
+// probability tile can be fed straight back as the K-operand of the next
+// product with 16-byte LDS reads on the other operand.
+__device__ __forceinline__ int perm23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Row (within its 32-row block) held by accumulator register r of lane-half g
+// when operand rows were read in perm23 order.
+__device__ __forceinline__ int acc_row(int r, int g) { return ((r >> 3) << 4) + (g << 3) + (r & 7); }
+
+// Value of x in the lane 32 positions away, combined with x by max / add.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace fa

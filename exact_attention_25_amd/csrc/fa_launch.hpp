@@ -1,0 +1,42 @@
+// fa_launch.hpp -- host-side launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t N;
+  int BH;          // B * H
+  int n_qtiles;    // ceil(N / fwd_block_m())
+  float scale_log2;  // scale * log2(e)
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;      // workspace: [B*H*N] FP32
+  int64_t N;
+  int BH;
+  float scale;       // the caller's scale (for dQ, dK)
+  float scale_log2;  // scale * log2(e)
+};
+
+int fwd_block_m();
+hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,120 @@
+/*
+ * fa.h -- C ABI of libfa: exact scaled-dot-product attention on MI355X (gfx950).
+ *
+ * The operation (cited by page title and section):
+ *   Forward:  O = softmax(scale * Q K^T + M) V, with the causal mask
+ *             M_ij = -inf for j > i ("CUDA FlashAttention: from online softmax
+ *             to the long-sequence IO limit", §1), computed tile by tile with
+ *             the online-softmax recurrence (same page, §4; "Why FlashAttention
+ *             does not need to store the attention matrix", §3.2) so that the
+ *             score and probability matrices never reach device memory.  The
+ *             per-row log-sum-exp LSE_i = m_i + ln(l_i) (natural log) is
+ *             emitted for the backward pass ("Why FlashAttention ...", §3.2
+ *             and §3.3).
+ *   Backward: recomputes P = exp(scale * Q K^T + M - LSE) tile by tile and
+ *             forms dV = P^T dO, dP = dO V^T, dS = P * (dP - Delta),
+ *             dQ = scale * dS K, dK = scale * dS^T Q, with
+ *             Delta_i = sum_d dO_id O_id ("Why FlashAttention ...", §3.3;
+ *             "FlashAttention algorithm details", §4.3.1-4.3.2; the
+ *             correction term of "FlashAttention dataflow and engineering
+ *             validation on MI50", §3.3).
+ *
+ * Memory and layout (all entry points):
+ *   - Every tensor pointer is a DEVICE pointer into memory the caller owns.
+ *     The library never allocates, frees or synchronises; it enqueues kernels
+ *     on `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *   - Q, K, V, O, dO, dQ, dK, dV: contiguous row-major [B, H, N, D], D fastest,
+ *     element type fp16 (FA_FP16) or bf16 (FA_BF16), 16-byte aligned base.
+ *   - LSE and the backward workspace: contiguous FP32 [B, H, N], 16-byte
+ *     aligned.
+ *   - Outputs must not alias inputs or each other.
+ *   - Supported: D in {64, 128}; N a positive multiple of 64; B, H >= 1;
+ *     B*H*N*D < 2^31 * 64; scale finite and > 0.  Anything else is rejected
+ *     with an error code before any work is enqueued -- never silently
+ *     computed ("CUDA FlashAttention ...", §9: unsupported shapes fall back
+ *     explicitly).
+ *   - Numerics: products on fp16/bf16 MFMA with FP32 accumulation; running
+ *     max, sum and output accumulators in FP32 ("CUDA FlashAttention ...", §2);
+ *     outputs rounded to the storage type with round-to-nearest-even.
+ *
+ * Error convention: every entry point returns FA_OK (0) or a positive
+ * fa_status.  Argument errors are detected before anything is launched.
+ * FA_ERR_HIP means a launch was rejected by the runtime; faults during
+ * execution surface at the caller's next synchronisation of `stream`.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = 2,       /* B, H or N <= 0, or the index space is too large     */
+  FA_ERR_UNSUPPORTED = 3, /* D, dtype, causal flag, N % 64 or scale unsupported  */
+  FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
+  FA_ERR_WORKSPACE = 5,   /* backward workspace missing or smaller than needed   */
+  FA_ERR_HIP = 6          /* the HIP runtime rejected a launch                   */
+} fa_status;
+
+typedef enum fa_dtype { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * fa_fwd -- attention forward.
+ *   q, k, v : inputs [B,H,N,D] of `dtype`.
+ *   o       : output [B,H,N,D] of `dtype`, O = softmax(scale*QK^T + M) V.
+ *   lse     : output FP32 [B,H,N], natural-log log-sum-exp of each score row
+ *             (with the mask applied).
+ *   causal  : 0 = no mask, 1 = square top-left causal mask (key j visible to
+ *             query i iff j <= i).  Tiles wholly above the diagonal are
+ *             skipped ("Why FlashAttention ...", §4.5).
+ *   scale   : multiplies Q K^T; callers pass 1/sqrt(D) for standard attention.
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t N, int64_t D,
+           int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one FP32
+ * value per query row for Delta_i = rowsum(dO_i * O_i), i.e. 4*B*H*N, rounded
+ * up to 256.  Returns 0 for arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
+                              int causal, int dtype);
+
+/*
+ * fa_bwd -- attention backward by recomputation.
+ *   q, k, v, o, lse : the forward's inputs and outputs (o and lse exactly as
+ *                     fa_fwd wrote them).
+ *   dout            : upstream gradient dL/dO [B,H,N,D] of `dtype`.
+ *   dq, dk, dv      : outputs [B,H,N,D] of `dtype`; fully overwritten.
+ *   workspace       : device scratch of at least fa_bwd_workspace_bytes(...)
+ *                     bytes, owned by the caller; its contents on entry are
+ *                     ignored and on return are unspecified.
+ *   other arguments : as for fa_fwd and with the same values.
+ * Three kernels run in order on `stream`: Delta, then dK/dV (outer loop over
+ * key tiles), then dQ (outer loop over query tiles).  No atomics are used, so
+ * results are bitwise reproducible.
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout,
+           void* dq, void* dk, void* dv,
+           int64_t B, int64_t H, int64_t N, int64_t D,
+           int causal, float scale, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_status_str -- a static, human-readable name for a status code. */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -42,19 +42,21 @@ def _check4(*arrays):
 # ---------------------------------------------------------------------------
 # Plain definition: two-pass safe softmax over complete, materialised rows.
 # ---------------------------------------------------------------------------
-def _scores_block(qh, kh, i0, i1, causal, scale):
-    """Rows i0..i1-1 of S = scale * Q K^T with the causal -inf mask applied.
+def _scores_block(qh, kh, i0, i1, causal, scale, rows=None):
+    """Score rows S = scale * Q K^T with the causal -inf mask applied.
 
-    With ``causal`` the rows only ever see keys 0..i1-1, so the block is
+    Rows are query indices i0..i1-1, or the explicit index array ``rows``.
+    With ``causal`` the block only ever sees keys 0..max(row), so it is
     truncated there; the truncated columns would all be -inf anyway.
     Definition: [FA-CUDA] §1 (S = QK^T/sqrt(D) + M, M_ij = -inf for j > i).
     """
-    nk = i1 if causal else kh.shape[0]
-    s = scale * (qh[i0:i1] @ kh[:nk].T)
+    if rows is None:
+        rows = np.arange(i0, i1)
+    nk = int(rows.max()) + 1 if causal else kh.shape[0]
+    s = scale * (qh[rows] @ kh[:nk].T)
     if causal:
-        rows = np.arange(i0, i1)[:, None]
         cols = np.arange(nk)[None, :]
-        s = np.where(cols > rows, NEG_INF, s)
+        s = np.where(cols > rows[:, None], NEG_INF, s)
     return s, nk
 
 
@@ -67,7 +69,7 @@ def _safe_softmax_rows(s):
     return e / l[:, None], m, l
 
 
-def attention_forward(q, k, v, causal, scale, row_block=256):
+def attention_forward(q, k, v, causal, scale, row_block=256, rows=None):
     """O = softmax(scale * Q K^T + M) V and LSE, by the plain definition.
 
     For every (b, h) and every block of ``row_block`` query rows the complete
@@ -76,22 +78,27 @@ def attention_forward(q, k, v, causal, scale, row_block=256):
     Sources: [FA-CUDA] §1 (definition), [FA-WHY] §3.1 (safe softmax) and
     §3.2 (LSE = m + log l).
 
-    Returns (O, LSE) as float64 arrays of shape [B,H,N,D] and [B,H,N].
+    ``rows``: optional 1-D array of query indices; then only those rows are
+    computed (for every head) and the outputs have len(rows) in place of N.
+
+    Returns (O, LSE) as float64 arrays of shape [B,H,R,D] and [B,H,R].
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     _check4(q, k, v)
     B, H, N, D = q.shape
-    o = np.empty((B, H, N, D))
-    lse = np.empty((B, H, N))
+    sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = sel.shape[0]
+    o = np.empty((B, H, R, D))
+    lse = np.empty((B, H, R))
     for b in range(B):
         for h in range(H):
             qh, kh, vh = q[b, h], k[b, h], v[b, h]
-            for i0 in range(0, N, row_block):
-                i1 = min(N, i0 + row_block)
-                s, nk = _scores_block(qh, kh, i0, i1, causal, scale)
+            for r0 in range(0, R, row_block):
+                r1 = min(R, r0 + row_block)
+                s, nk = _scores_block(qh, kh, 0, 0, causal, scale, rows=sel[r0:r1])
                 p, m, l = _safe_softmax_rows(s)
-                o[b, h, i0:i1] = p @ vh[:nk]
-                lse[b, h, i0:i1] = m + np.log(l)
+                o[b, h, r0:r1] = p @ vh[:nk]
+                lse[b, h, r0:r1] = m + np.log(l)
     return o, lse
 
 

@@ -296,3 +296,14 @@ def test_constant_keys_give_zero_dq():
     k = np.tile(_rand(83, d), (1, 1, n, 1))
     dq, _, _ = attention_backward(q, k, v, do, True, 0.5)
     assert np.abs(dq).max() < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_selected_rows_match_brute_force(causal):
+    n, d = 8, 3
+    q, k, v = _rand(90, n, d), _rand(91, n, d), _rand(92, n, d)
+    rows = np.array([7, 0, 3, 3, 5])
+    o, lse = attention_forward(_heads(q), _heads(k), _heads(v), causal, 0.8, rows=rows, row_block=2)
+    ob, lb = brute_force_forward(q.tolist(), k.tolist(), v.tolist(), causal, 0.8)
+    assert np.abs(o[0, 0] - np.array(ob)[rows]).max() < 1e-14
+    assert np.abs(lse[0, 0] - np.array(lb)[rows]).max() < 1e-14
