@@ -59,14 +59,16 @@ __device__ __forceinline__ uint32_t pack2(float a, float b);
 
 template <>
 __device__ __forceinline__ uint32_t pack2<Fp16>(float a, float b) {
-  _Float16 x = (_Float16)a, y = (_Float16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = {(_Float16)a, (_Float16)b};  // one v_cvt_pk_f16_f32
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <>
 __device__ __forceinline__ uint32_t pack2<Bf16>(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 v = {(__bf16)a, (__bf16)b};  // one v_cvt_pk_bf16_f32
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Eight floats (elements lo..lo+7 of an accumulator) -> one MFMA operand.
@@ -106,5 +108,9 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave-uniform votes (every lane of the wave is active where these are used).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+__device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }
 
 }  // namespace fa

@@ -34,6 +34,8 @@ namespace {
 constexpr int kFwdBM = 128;  // queries per workgroup
 constexpr int kFwdBN = 64;   // keys per tile
 constexpr int kFwdThreads = 256;
+constexpr float kLazy = 8.0f;         // max probability 2^8 between rescales
+constexpr float kFastLimit = 4096.0f; // |scale*log2e*S| below this: one-FMA exponent
 
 template <int D, bool CAUSAL, class T>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max of scale*log2(e)*S
+  float r_raw = -INFINITY;  // reference max, in raw (unscaled) score units
   float l_run = 0.f;        // this lane's part of the running sum
 
   const int n_kt_all = (int)(N / BN);
@@ -160,10 +162,39 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);  // 0 while m_run is -inf
+    mx = xhalf_max(mx);  // raw max of this row over the tile
+
+    // The reference max r_raw is always one of the raw scores (exact).  In
+    // the usual case the exponent is one FMA, s*c2 - RN(r_raw*c2), and the
+    // reference is only raised when the tile max exceeds it by more than
+    // kLazy in log2 units, so probabilities stay below 2^kLazy and the O/l
+    // rescale is skipped on most tiles; the result is unchanged because O and
+    // l always share the same reference.  When scaled scores are so large
+    // that RN(r_raw*c2) is off by a meaningful amount (|.| >= kFastLimit), the
+    // scores are first shifted by r_raw in raw units, where the difference is
+    // exact for scores near the max, and the same FMA then scales them.
+    const float mc_tile = mx * c2;
+    float mref = r_raw * c2;
+    const bool fast_ok = (fabsf(mc_tile) < kFastLimit || mc_tile == -INFINITY) &&
+                         (fabsf(mref) < kFastLimit || mref == -INFINITY);
+    const bool exact = !wave_all(fast_ok);
+    if (exact || wave_any(mc_tile > mref + kLazy)) {
+      const float r_new = fmaxf(r_raw, mx);
+      const float lg = exact ? (r_raw - r_new) * c2 : mref - r_new * c2;
+      const float alpha = (r_raw == -INFINITY) ? 0.f : fast_exp2(lg);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+      r_raw = r_new;
+      mref = r_raw * c2;
+    }
+    float m_use = (mref == -INFINITY) ? 0.f : mref;
+    if (exact) {
+      const float ru = (r_raw == -INFINITY) ? 0.f : r_raw;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] -= ru;
+      m_use = 0.f;
+    }
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -173,10 +204,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         s[kb][r] = p;
         lsum += p;
       }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+    l_run += lsum;
 
     // O^T += V^T P^T, 16 keys per step: step t uses keys 16t .. 16t+15, which
     // are accumulator registers 8*(t%2) .. +7 of block t/2 (see acc_row).
@@ -204,7 +232,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
       w[1] = pack2<T>(oacc[db][rq * 4 + 2] * inv, oacc[db][rq * 4 + 3] * inv);
       *(u32x2*)(Orow + db * 32 + rq * 8 + g * 4) = w;
     }
-  if (g == 0) a.lse[(int64_t)bh * N + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+  if (g == 0) a.lse[(int64_t)bh * N + my_q] = (r_raw * c2 + __log2f(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, class T>
