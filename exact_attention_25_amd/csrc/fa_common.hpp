@@ -109,6 +109,31 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS copies and transposing LDS reads (gfx950).
+// ---------------------------------------------------------------------------
+// global_load_lds_dwordx4: every lane fetches 16 bytes from its own global
+// address; lane l's bytes land at lds_wave_base + 16*l.  lds_wave_base must
+// be the same for the whole wave.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+// Wait until this wave's outstanding global loads (including LDS-bound ones)
+// have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane j points at four
+// consecutive 16-bit values R_j[0..3]; lane i receives R_{4k + i/4}[i % 4]
+// for k = 0..3.  Pointing lane j at row (k0 + j/4), columns c0 + 4*(j%4)
+// .. +3 of a row-major tile hands lane i the column c0 + i of rows k0..k0+3:
+// a transposed MFMA operand read straight from a row-major tile.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lds_addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Wave-uniform votes (every lane of the wave is active where these are used).
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 __device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }

@@ -13,10 +13,12 @@
 // Work decomposition (one workgroup = 4 waves = 128 queries of one head):
 //  * Each wave owns 32 queries.  Their Q rows stay in VGPRs for the whole
 //    pass as the B operand of S^T = K Q^T (32 keys x 32 queries per MFMA).
-//  * Keys and values stream in tiles of 64 through LDS.  K is stored row
-//    major (swizzled); V is stored transposed (V^T, keys contiguous) so that
-//    O^T = V^T P^T reads 16-byte operand fragments.  While a tile is being
-//    used, the next one is already in flight from HBM into registers.
+//  * Keys and values stream in tiles of 64 keys straight from HBM into a
+//    double-buffered LDS ring (global_load_lds_dwordx4: no VGPR staging), one
+//    workgroup barrier per tile.  Both tiles stay row-major with an XOR
+//    swizzle of 16-byte chunks; K fragments are read with ds_read_b128 and
+//    the V^T fragments of O^T = V^T P^T with the transposing
+//    ds_read_b64_tr_b16, so V is never transposed in memory.
 //  * Computing S^T puts one query per lane (two lanes per query, 32 keys
 //    each), so the row max is an in-lane reduction plus one cross-half swap,
 //    and the row sum needs no cross-lane step until the epilogue.
@@ -37,24 +39,30 @@ constexpr int kFwdThreads = 256;
 constexpr float kLazy = 8.0f;         // max probability 2^8 between rescales
 constexpr float kFastLimit = 4096.0f; // |scale*log2e*S| below this: one-FMA exponent
 
+// Physical 16-byte-chunk index of (row r, chunk c) in a V tile with RC chunks
+// per row.  The XOR uses even values 2*(r & m), so the four consecutive rows
+// and two adjacent chunks touched by one 16-lane transposed read land on
+// eight distinct chunk positions (no bank conflicts).
+template <int RC>
+__device__ __forceinline__ int v_chunk(int r, int c) {
+  return r * RC + (c ^ ((r & (RC == 16 ? 7 : 3)) << 1));
+}
+
 template <int D, bool CAUSAL, class T>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   constexpr int BM = kFwdBM, BN = kFwdBN, NT = kFwdThreads;
-  constexpr int KCH = D / 8;             // 16-byte chunks per K row
-  constexpr int K_CHUNKS = BN * KCH;     // chunks per K tile
-  constexpr int VCH = BN / 8;            // 16-byte chunks per V^T row
-  constexpr int KPT = K_CHUNKS / NT;     // K chunks loaded per thread
-  constexpr int DV = (BN * D) / (8 * NT);  // V columns per thread (8 keys each)
-  constexpr int DGROUPS = D / DV;        // threads per group of 8 keys
-  static_assert(KPT * NT == K_CHUNKS, "K tile split");
-  static_assert(DGROUPS * (BN / 8) == NT, "V tile split");
-  static_assert(DV == 2 || DV == 4, "V column split");
+  constexpr int RC = D / 8;              // 16-byte chunks per row
+  constexpr int TC = BN * RC;            // chunks per K or V tile
+  constexpr int LPT = TC / NT;           // direct copies per thread per tile
+  static_assert(LPT * NT == TC, "tile split");
 
-  __shared__ u32x4 lds_k[K_CHUNKS];
-  __shared__ u32x4 lds_vt[D * VCH];
+  // Two K and two V tile buffers as separate LDS objects, so the compiler
+  // can tell reads of one buffer from the copies in flight into the other.
+  __shared__ u32x4 lds_k0[TC], lds_k1[TC], lds_v0[TC], lds_v1[TC];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, g = lane >> 5;
 
   const int64_t N = a.N;
@@ -86,55 +94,46 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const int n_kt_all = (int)(N / BN);
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
 
-  // Next tile in flight: K chunks and 8 keys x DV columns of V.
-  const int dg = tid % DGROUPS, kg = tid / DGROUPS;
-  u32x4 kreg[KPT];
-  uint32_t vreg[8][DV / 2];
-
-  auto load_tile = [&](int kt) {
+  // Per-lane source offsets (in elements, within a tile) of this thread's
+  // direct copies: copy i of wave w fills LDS chunks i*NT + 64w + lane.
+  int ksrc[LPT], vsrc[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int p = i * NT + wave * 64 + lane;
+    ksrc[i] = swz(p) * 8;  // swz is its own inverse
+    const int r = p / RC;
+    vsrc[i] = r * D + ((p % RC) ^ ((r & (RC == 16 ? 7 : 3)) << 1)) * 8;
+  }
+  auto load_tile = [&](int kt, u32x4* kdst, u32x4* vdst) {
     const uint16_t* Kt = Kh + (int64_t)kt * BN * D;
+    const uint16_t* Vt = Vh + (int64_t)kt * BN * D;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) kreg[i] = *(const u32x4*)(Kt + (tid + i * NT) * 8);
-    const uint16_t* Vt = Vh + (int64_t)kt * BN * D + (int64_t)(kg * 8) * D + dg * DV;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if constexpr (DV == 4) {
-        u32x2 x = *(const u32x2*)(Vt + r * D);
-        vreg[r][0] = x[0];
-        vreg[r][1] = x[1];
-      } else {
-        vreg[r][0] = *(const uint32_t*)(Vt + r * D);
-      }
+    for (int i = 0; i < LPT; ++i) {
+      copy16_to_lds(Kt + ksrc[i], kdst + i * NT + wave * 64);
+      copy16_to_lds(Vt + vsrc[i], vdst + i * NT + wave * 64);
     }
   };
 
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) lds_k[swz(tid + i * NT)] = kreg[i];
-    // transpose 8 keys x DV columns into DV rows of V^T (8 keys each)
-#pragma unroll
-    for (int j = 0; j < DV; ++j) {
-      u32x4 w;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        uint32_t lo = vreg[2 * p][j >> 1], hi = vreg[2 * p + 1][j >> 1];
-        w[p] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      const int d = dg * DV + j;
-      lds_vt[swz(d * VCH + kg)] = w;
-    }
-  };
+  // Lane-constant parts of the transposed V reads: lane j of 16-lane group q
+  // reads row 8g + j/4 (+4 for the second half), columns d0 + 4*(j%4), with
+  // d0 = 32*db + 16*(q%2).
+  const int vj = lane & 15, vq = lane >> 4;
+  const int v_row0 = 8 * g + (vj >> 2);
+  const int v_col = 16 * (vq & 1) + 4 * (vj & 3);  // + 32*db
 
   const float c2 = a.scale_log2;
-  load_tile(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+
+  // One key tile: wait for its copies, start the next tile's copies into the
+  // other buffer pair, then compute from this one.
+  auto step = [&](int kt, const u32x4* __restrict__ Kl, const u32x4* __restrict__ Vlv, u32x4* knext,
+                  u32x4* vnext) {
+    wait_vmem();      // this wave's copies of tile kt have landed
+    __syncthreads();  // everyone's have; everyone is done with tile kt-1
+    if (kt + 1 < n_kt) load_tile(kt + 1, knext, vnext);
+    const char* __restrict__ Vl = (const char*)Vlv;
 
     const int k0 = kt * BN;
-    if (!active || (CAUSAL && k0 > q0w + 31)) continue;  // nothing visible
+    if (!active || (CAUSAL && k0 > q0w + 31)) return;  // nothing visible
 
     // S^T = K Q^T for 64 keys (two 32-key blocks) x 32 queries.
     f32x16 s[2];
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
       const int krow = kb * 32 + perm23(ql);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const u32x4 kf = lds_k[swz(krow * KCH + c * 2 + g)];
+        const u32x4 kf = Kl[swz(krow * RC + c * 2 + g)];
         s[kb] = mfma32<T>(kf, qf[c], s[kb]);
       }
     }
@@ -213,10 +212,19 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
       const u32x4 pf = pack8<T>(s[t >> 1], (t & 1) * 8);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const u32x4 vf = lds_vt[swz((db * 32 + ql) * VCH + 2 * t + g)];
-        oacc[db] = mfma32<T>(vf, pf, oacc[db]);
+        const int col = db * 32 + v_col;
+        const int r0 = 16 * t + v_row0;
+        const u32x2 lo = lds_read_tr16(Vl + v_chunk<RC>(r0, col >> 3) * 16 + (col & 7) * 2);
+        const u32x2 hi = lds_read_tr16(Vl + v_chunk<RC>(r0 + 4, col >> 3) * 16 + (col & 7) * 2);
+        oacc[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, oacc[db]);
       }
     }
+  };
+
+  load_tile(0, lds_k0, lds_v0);
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    step(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+    if (kt + 1 < n_kt) step(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
   }
 
   if (!active) return;
