@@ -94,23 +94,34 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const int n_kt_all = (int)(N / BN);
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
 
-  // Per-lane source offsets (in elements, within a tile) of this thread's
-  // direct copies: copy i of wave w fills LDS chunks i*NT + 64w + lane.
-  int ksrc[LPT], vsrc[LPT];
+  // Direct copies: copy i of wave w fills LDS chunks i*NT + 64w + lane.  The
+  // per-lane source offsets (elements within a tile) differ between copies
+  // only by a constant, because the swizzles depend on low row bits only.
+  const int p0 = wave * 64 + lane;
+  const int ksrc0 = swz(p0) * 8;
+  const int vr0 = p0 / RC;
+  const int vsrc0 = vr0 * D + ((p0 % RC) ^ ((vr0 & (RC == 16 ? 7 : 3)) << 1)) * 8;
+  auto load_k = [&](int kt, u32x4* dst) {
+    const uint16_t* src = Kh + (int64_t)kt * BN * D + ksrc0;
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int p = i * NT + wave * 64 + lane;
-    ksrc[i] = swz(p) * 8;  // swz is its own inverse
-    const int r = p / RC;
-    vsrc[i] = r * D + ((p % RC) ^ ((r & (RC == 16 ? 7 : 3)) << 1)) * 8;
-  }
-  auto load_tile = [&](int kt, u32x4* kdst, u32x4* vdst) {
-    const uint16_t* Kt = Kh + (int64_t)kt * BN * D;
-    const uint16_t* Vt = Vh + (int64_t)kt * BN * D;
+    for (int i = 0; i < LPT; ++i) copy16_to_lds(src + i * NT * 8, dst + i * NT + wave * 64);
+  };
+  auto load_v = [&](int kt, u32x4* dst) {
+    const uint16_t* src = Vh + (int64_t)kt * BN * D + vsrc0;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      copy16_to_lds(Kt + ksrc[i], kdst + i * NT + wave * 64);
-      copy16_to_lds(Vt + vsrc[i], vdst + i * NT + wave * 64);
+    for (int i = 0; i < LPT; ++i) copy16_to_lds(src + i * NT * 8, dst + i * NT + wave * 64);
+  };
+
+  // S^T = K Q^T for one 64-key tile: two 32-key blocks, K rows read in
+  // perm23 order so that register r of lane-half g holds key acc_row(r, g).
+  const int krow = perm23(ql);
+  auto scores = [&](const u32x4* __restrict__ Kl, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        s[kb] = mfma32<T>(Kl[swz((kb * 32 + krow) * RC + c * 2 + g)], qf[c], s[kb]);
     }
   };
 
@@ -119,34 +130,24 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   // d0 = 32*db + 16*(q%2).
   const int vj = lane & 15, vq = lane >> 4;
   const int v_row0 = 8 * g + (vj >> 2);
-  const int v_col = 16 * (vq & 1) + 4 * (vj & 3);  // + 32*db
-
+  const int v_col = 16 * (vq & 1) + 4 * (vj & 3);
   const float c2 = a.scale_log2;
 
-  // One key tile: wait for its copies, start the next tile's copies into the
-  // other buffer pair, then compute from this one.
-  auto step = [&](int kt, const u32x4* __restrict__ Kl, const u32x4* __restrict__ Vlv, u32x4* knext,
-                  u32x4* vnext) {
-    wait_vmem();      // this wave's copies of tile kt have landed
-    __syncthreads();  // everyone's have; everyone is done with tile kt-1
-    if (kt + 1 < n_kt) load_tile(kt + 1, knext, vnext);
-    const char* __restrict__ Vl = (const char*)Vlv;
+  // One key tile kt, software-pipelined: on entry s_cur holds the raw scores
+  // of tile kt (computed during the previous tile); while the softmax of
+  // tile kt runs on the vector ALUs, the score MFMAs of tile kt+1 (its K is
+  // already in LDS) are issued into s_nxt.  K therefore streams one tile
+  // ahead of V: the copies started here are K for tile kt+2 (into the buffer
+  // that held K of tile kt) and V for tile kt+1.
+  auto step = [&](int kt, const u32x4* __restrict__ Knext, const u32x4* __restrict__ Vcur, u32x4* kdst,
+                  u32x4* vdst, f32x16 (&s)[2], f32x16 (&s_nxt)[2]) {
+    wait_vmem();      // K of tile kt+1 and V of tile kt have landed (this wave's part)
+    __syncthreads();  // ... everyone's part; everyone is done with tile kt-1
+    if (kt + 2 < n_kt) load_k(kt + 2, kdst);
+    if (kt + 1 < n_kt) load_v(kt + 1, vdst);
 
     const int k0 = kt * BN;
     if (!active || (CAUSAL && k0 > q0w + 31)) return;  // nothing visible
-
-    // S^T = K Q^T for 64 keys (two 32-key blocks) x 32 queries.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int krow = kb * 32 + perm23(ql);
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const u32x4 kf = Kl[swz(krow * RC + c * 2 + g)];
-        s[kb] = mfma32<T>(kf, qf[c], s[kb]);
-      }
-    }
 
     if (CAUSAL && k0 + BN - 1 > q0w) {  // diagonal tile: mask before the max
 #pragma unroll
@@ -155,7 +156,6 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r)
           if (k0 + kb * 32 + acc_row(r, g) > my_q) s[kb][r] = -INFINITY;
     }
-
     float mx = s[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
@@ -167,11 +167,12 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     // the usual case the exponent is one FMA, s*c2 - RN(r_raw*c2), and the
     // reference is only raised when the tile max exceeds it by more than
     // kLazy in log2 units, so probabilities stay below 2^kLazy and the O/l
-    // rescale is skipped on most tiles; the result is unchanged because O and
-    // l always share the same reference.  When scaled scores are so large
-    // that RN(r_raw*c2) is off by a meaningful amount (|.| >= kFastLimit), the
-    // scores are first shifted by r_raw in raw units, where the difference is
-    // exact for scores near the max, and the same FMA then scales them.
+    // rescale is skipped on most tiles; the result is unchanged because O
+    // and l always share the same reference.  When scaled scores are so
+    // large that RN(r_raw*c2) is off by a meaningful amount
+    // (|.| >= kFastLimit), the scores are first shifted by r_raw in raw
+    // units, where the difference is exact for scores near the max, and the
+    // same FMA then scales them.
     const float mc_tile = mx * c2;
     float mref = r_raw * c2;
     const bool fast_ok = (fabsf(mc_tile) < kFastLimit || mc_tile == -INFINITY) &&
@@ -194,37 +195,54 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb) s[kb] -= ru;
       m_use = 0.f;
     }
+
+    // Scores of the next tile (its K is resident) -- independent of the
+    // softmax below, so the two overlap.  On a wave's last tile the MFMAs
+    // read a stale buffer and the result is discarded.
+    scores(Knext, s_nxt);
+
+    // P = exp2(s*c2 - m), packed to fp16/bf16 as the B operand of O^T += V^T P^T.
+    u32x4 pf[BN / 16];
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(s[kb][r], c2, -m_use));
-        s[kb][r] = p;
-        lsum += p;
-      }
-    l_run += lsum;
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c2, -m_use));
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t) pf[t] = pack8<T>(s[t >> 1], (t & 1) * 8);
 
     // O^T += V^T P^T, 16 keys per step: step t uses keys 16t .. 16t+15, which
     // are accumulator registers 8*(t%2) .. +7 of block t/2 (see acc_row).
+    const char* __restrict__ Vl = (const char*)Vcur;
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
-      const u32x4 pf = pack8<T>(s[t >> 1], (t & 1) * 8);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int col = db * 32 + v_col;
         const int r0 = 16 * t + v_row0;
         const u32x2 lo = lds_read_tr16(Vl + v_chunk<RC>(r0, col >> 3) * 16 + (col & 7) * 2);
         const u32x2 hi = lds_read_tr16(Vl + v_chunk<RC>(r0 + 4, col >> 3) * 16 + (col & 7) * 2);
-        oacc[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, oacc[db]);
+        oacc[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[t], oacc[db]);
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lsum += s[kb][r];
+    l_run += lsum;
   };
 
-  load_tile(0, lds_k0, lds_v0);
+  // Prologue: K and V of tile 0, K of tile 1, scores of tile 0.
+  f32x16 sA[2], sB[2];
+  load_k(0, lds_k0);
+  load_v(0, lds_v0);
+  if (n_kt > 1) load_k(1, lds_k1);
+  wait_vmem();
+  __syncthreads();
+  if (active) scores(lds_k0, sA);
   for (int kt = 0; kt < n_kt; kt += 2) {
-    step(kt, lds_k0, lds_v0, lds_k1, lds_v1);
-    if (kt + 1 < n_kt) step(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+    step(kt, lds_k1, lds_v0, lds_k0, lds_v1, sA, sB);
+    if (kt + 1 < n_kt) step(kt + 1, lds_k0, lds_v1, lds_k1, lds_v0, sB, sA);
   }
 
   if (!active) return;
