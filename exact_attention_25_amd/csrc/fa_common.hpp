@@ -71,6 +71,22 @@ __device__ __forceinline__ uint32_t pack2<Bf16>(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed pair of 16-bit values, in FP32 (one v_dot2).
+template <class T>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc);
+
+template <>
+__device__ __forceinline__ float add_pair<Fp16>(uint32_t w, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), h2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+}
+
+template <>
+__device__ __forceinline__ float add_pair<Bf16>(uint32_t w, float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), b2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+}
+
 // Eight floats (elements lo..lo+7 of an accumulator) -> one MFMA operand.
 template <class T>
 __device__ __forceinline__ u32x4 pack8(const f32x16& s, int lo) {

@@ -201,15 +201,28 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     // read a stale buffer and the result is discarded.
     scores(Knext, s_nxt);
 
-    // P = exp2(s*c2 - m), packed to fp16/bf16 as the B operand of O^T += V^T P^T.
+    // P = exp2(s*c2 - m), packed to fp16/bf16 (round to nearest even) as the
+    // B operand of O^T += V^T P^T.  For fp16 the row sum l adds the same
+    // rounded probabilities that weight V, pairwise in FP32 (v_dot2 with
+    // ones); bf16 keeps only 8 bits, so there l sums the FP32 values.
     u32x4 pf[BN / 16];
-    float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c2, -m_use));
+    float lsum = 0.f;
 #pragma unroll
-    for (int t = 0; t < BN / 16; ++t) pf[t] = pack8<T>(s[t >> 1], (t & 1) * 8);
+    for (int t = 0; t < BN / 16; ++t) {
+      pf[t] = pack8<T>(s[t >> 1], (t & 1) * 8);
+      if constexpr (T::id == Fp16::id) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lsum = add_pair<T>(pf[t][e], lsum);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lsum += s[t >> 1][(t & 1) * 8 + e];
+      }
+    }
+    l_run += lsum;
 
     // O^T += V^T P^T, 16 keys per step: step t uses keys 16t .. 16t+15, which
     // are accumulator registers 8*(t%2) .. +7 of block t/2 (see acc_row).
@@ -225,11 +238,6 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         oacc[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[t], oacc[db]);
       }
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) lsum += s[kb][r];
-    l_run += lsum;
   };
 
   // Prologue: K and V of tile 0, K of tile 1, scores of tile 0.
