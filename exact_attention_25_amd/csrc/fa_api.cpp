@@ -61,8 +61,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.lse = lse;
   a.N = N;
   a.BH = static_cast<int>(B * H);
-  const int bm = fa::fwd_block_m();
-  a.n_qtiles = static_cast<int>((N + bm - 1) / bm);
+  a.n_qtiles = 0;  // set by the launcher from its tile shape
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = fa::launch_fwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

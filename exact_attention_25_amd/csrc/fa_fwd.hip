@@ -10,9 +10,11 @@
 // ...", §6).  Tiles wholly above the causal diagonal are never visited
 // ("Why FlashAttention does not need to store the attention matrix", §4.5).
 //
-// Work decomposition (one workgroup = 4 waves = 128 queries of one head):
-//  * Each wave owns 32 queries.  Their Q rows stay in VGPRs for the whole
-//    pass as the B operand of S^T = K Q^T (32 keys x 32 queries per MFMA).
+// Work decomposition (one workgroup = 4 waves of one head):
+//  * Each wave owns QB blocks of 32 queries (QB = 1 or 2).  Their Q rows stay
+//    in VGPRs for the whole pass as the B operand of S^T = K Q^T (32 keys x
+//    32 queries per MFMA).  With QB = 2 every K or V^T fragment read from
+//    LDS feeds two independent MFMAs, halving LDS traffic per FLOP.
 //  * Keys and values stream in tiles of 64 keys straight from HBM into a
 //    double-buffered LDS ring (global_load_lds_dwordx4: no VGPR staging), one
 //    workgroup barrier per tile.  Both tiles stay row-major with an XOR
@@ -22,7 +24,9 @@
 //  * Computing S^T puts one query per lane (two lanes per query, 32 keys
 //    each), so the row max is an in-lane reduction plus one cross-half swap,
 //    and the row sum needs no cross-lane step until the epilogue.
-//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA.
+//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  While
+//    the softmax of tile j runs, the score MFMAs of tile j+1 are issued (K
+//    streams one tile ahead of V), so matrix and vector work overlap.
 //  * Workgroups are numbered heaviest-first for causal masks, and all query
 //    tiles of one head get workgroup ids congruent modulo 8, so they run on
 //    the same XCD and share its L2 for the re-streamed K/V.
@@ -33,11 +37,15 @@ namespace fa {
 
 namespace {
 
-constexpr int kFwdBM = 128;  // queries per workgroup
 constexpr int kFwdBN = 64;   // keys per tile
+// Query blocks per wave.  Two blocks halve LDS reads per MFMA but need about
+// 420 live registers, i.e. one wave per SIMD; measured on MI355X that loses
+// far more latency hiding than it saves (causal D=128: 210 vs 850 TFLOP/s),
+// so the shipped tiling is one block per wave, two waves per SIMD.
+constexpr int kFwdQB = 1;
 constexpr int kFwdThreads = 256;
-constexpr float kLazy = 8.0f;         // max probability 2^8 between rescales
-constexpr float kFastLimit = 4096.0f; // |scale*log2e*S| below this: one-FMA exponent
+constexpr float kLazy = 8.0f;          // max probability 2^8 between rescales
+constexpr float kFastLimit = 4096.0f;  // |scale*log2e*S| below this: one-FMA exponent
 
 // Physical 16-byte-chunk index of (row r, chunk c) in a V tile with RC chunks
 // per row.  The XOR uses even values 2*(r & m), so the four consecutive rows
@@ -48,12 +56,18 @@ __device__ __forceinline__ int v_chunk(int r, int c) {
   return r * RC + (c ^ ((r & (RC == 16 ? 7 : 3)) << 1));
 }
 
-template <int D, bool CAUSAL, class T>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int BM = kFwdBM, BN = kFwdBN, NT = kFwdThreads;
+template <int QB>
+struct FwdShape {
+  static constexpr int BM = 32 * QB * (kFwdThreads / 64);  // queries per workgroup
+};
+
+template <int D, int QB, bool CAUSAL, class T>
+__global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdArgs a) {
+  constexpr int BM = FwdShape<QB>::BM, BN = kFwdBN, NT = kFwdThreads;
   constexpr int RC = D / 8;              // 16-byte chunks per row
   constexpr int TC = BN * RC;            // chunks per K or V tile
   constexpr int LPT = TC / NT;           // direct copies per thread per tile
+  constexpr int WQ = 32 * QB;            // queries per wave
   static_assert(LPT * NT == TC, "tile split");
 
   // Two K and two V tile buffers as separate LDS objects, so the compiler
@@ -74,22 +88,28 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const uint16_t* __restrict__ Kh = a.k + head;
   const uint16_t* __restrict__ Vh = a.v + head;
 
-  const int q0w = qt * BM + wave * 32;  // first query of this wave
+  const int q0w = qt * BM + wave * WQ;  // first query of this wave
   const bool active = q0w < N;          // N % 64 == 0: whole wave in or out
-  const int my_q = q0w + ql;
 
-  // Q^T operand fragments: lane (ql, g) holds Q[my_q][16c + 8g .. +8].
-  u32x4 qf[D / 16];
+  // Q^T operand fragments: lane (ql, g) of block qb holds
+  // Q[q0w + 32qb + ql][16c + 8g .. +8].
+  u32x4 qf[QB][D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    qf[c] = active ? *(const u32x4*)(Qh + (int64_t)my_q * D + c * 16 + g * 8) : u32x4{0, 0, 0, 0};
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qf[qb][c] = active ? *(const u32x4*)(Qh + (int64_t)(q0w + 32 * qb + ql) * D + c * 16 + g * 8)
+                         : u32x4{0, 0, 0, 0};
+
+  f32x16 oacc[QB][D / 32];
+  float r_raw[QB], l_run[QB];  // reference max (raw score units); this lane's part of l
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[qb][i] = f32x16{};
+    r_raw[qb] = -INFINITY;
+    l_run[qb] = 0.f;
   }
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  float r_raw = -INFINITY;  // reference max, in raw (unscaled) score units
-  float l_run = 0.f;        // this lane's part of the running sum
 
   const int n_kt_all = (int)(N / BN);
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
@@ -114,14 +134,19 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
 
   // S^T = K Q^T for one 64-key tile: two 32-key blocks, K rows read in
   // perm23 order so that register r of lane-half g holds key acc_row(r, g).
+  // Each K fragment feeds the QB query blocks.
   const int krow = perm23(ql);
-  auto scores = [&](const u32x4* __restrict__ Kl, f32x16 (&s)[2]) {
+  auto scores = [&](const u32x4* __restrict__ Kl, f32x16 (&s)[QB][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-        s[kb] = mfma32<T>(Kl[swz((kb * 32 + krow) * RC + c * 2 + g)], qf[c], s[kb]);
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const u32x4 kf = Kl[swz((kb * 32 + krow) * RC + c * 2 + g)];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32<T>(kf, qf[qb][c], s[qb][kb]);
+      }
     }
   };
 
@@ -133,35 +158,33 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const int v_col = 16 * (vq & 1) + 4 * (vj & 3);
   const float c2 = a.scale_log2;
 
-  // One key tile kt, software-pipelined: on entry s_cur holds the raw scores
-  // of tile kt (computed during the previous tile); while the softmax of
-  // tile kt runs on the vector ALUs, the score MFMAs of tile kt+1 (its K is
+  // One key tile kt, software-pipelined: on entry s holds the raw scores of
+  // tile kt (computed during the previous tile); while the softmax of tile
+  // kt runs on the vector ALUs, the score MFMAs of tile kt+1 (its K is
   // already in LDS) are issued into s_nxt.  K therefore streams one tile
   // ahead of V: the copies started here are K for tile kt+2 (into the buffer
   // that held K of tile kt) and V for tile kt+1.
   auto step = [&](int kt, const u32x4* __restrict__ Knext, const u32x4* __restrict__ Vcur, u32x4* kdst,
-                  u32x4* vdst, f32x16 (&s)[2], f32x16 (&s_nxt)[2]) {
+                  u32x4* vdst, f32x16 (&s)[QB][2], f32x16 (&s_nxt)[QB][2]) {
     wait_vmem();      // K of tile kt+1 and V of tile kt have landed (this wave's part)
     __syncthreads();  // ... everyone's part; everyone is done with tile kt-1
     if (kt + 2 < n_kt) load_k(kt + 2, kdst);
     if (kt + 1 < n_kt) load_v(kt + 1, vdst);
 
     const int k0 = kt * BN;
-    if (!active || (CAUSAL && k0 > q0w + 31)) return;  // nothing visible
+    if (!active || (CAUSAL && k0 > q0w + WQ - 1)) return;  // nothing visible
 
-    if (CAUSAL && k0 + BN - 1 > q0w) {  // diagonal tile: mask before the max
+    // Diagonal tile: mask before the max (a block wholly above its queries
+    // is masked entirely and contributes zero probabilities).
+    if (CAUSAL && k0 + BN - 1 > q0w) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (k0 + kb * 32 + acc_row(r, g) > my_q) s[kb][r] = -INFINITY;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (k0 + kb * 32 + acc_row(r, g) > q0w + 32 * qb + ql) s[qb][kb][r] = -INFINITY;
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = xhalf_max(mx);  // raw max of this row over the tile
 
     // The reference max r_raw is always one of the raw scores (exact).  In
     // the usual case the exponent is one FMA, s*c2 - RN(r_raw*c2), and the
@@ -173,27 +196,47 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     // (|.| >= kFastLimit), the scores are first shifted by r_raw in raw
     // units, where the difference is exact for scores near the max, and the
     // same FMA then scales them.
-    const float mc_tile = mx * c2;
-    float mref = r_raw * c2;
-    const bool fast_ok = (fabsf(mc_tile) < kFastLimit || mc_tile == -INFINITY) &&
-                         (fabsf(mref) < kFastLimit || mref == -INFINITY);
-    const bool exact = !wave_all(fast_ok);
-    if (exact || wave_any(mc_tile > mref + kLazy)) {
-      const float r_new = fmaxf(r_raw, mx);
-      const float lg = exact ? (r_raw - r_new) * c2 : mref - r_new * c2;
-      const float alpha = (r_raw == -INFINITY) ? 0.f : fast_exp2(lg);
-      l_run *= alpha;
+    float mx[QB], mref[QB];
+    bool fast_ok = true, need = false;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-      r_raw = r_new;
-      mref = r_raw * c2;
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = s[qb][0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, s[qb][1][r]);
+      mx[qb] = xhalf_max(m);  // raw max of this row over the tile
+      const float mc_tile = mx[qb] * c2;
+      mref[qb] = r_raw[qb] * c2;
+      fast_ok = fast_ok && (fabsf(mc_tile) < kFastLimit || mc_tile == -INFINITY) &&
+                (fabsf(mref[qb]) < kFastLimit || mref[qb] == -INFINITY);
+      need = need || (mc_tile > mref[qb] + kLazy);
     }
-    float m_use = (mref == -INFINITY) ? 0.f : mref;
-    if (exact) {
-      const float ru = (r_raw == -INFINITY) ? 0.f : r_raw;
+    const bool exact = !wave_all(fast_ok);
+    if (exact || wave_any(need)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] -= ru;
-      m_use = 0.f;
+      for (int qb = 0; qb < QB; ++qb) {
+        const float r_new = fmaxf(r_raw[qb], mx[qb]);
+        const float lg = exact ? (r_raw[qb] - r_new) * c2 : mref[qb] - r_new * c2;
+        const float alpha = (r_raw[qb] == -INFINITY) ? 0.f : fast_exp2(lg);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) oacc[qb][i] *= alpha;
+        r_raw[qb] = r_new;
+        mref[qb] = r_new * c2;
+      }
+    }
+    float m_use[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_use[qb] = (mref[qb] == -INFINITY) ? 0.f : mref[qb];
+    if (exact) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float ru = (r_raw[qb] == -INFINITY) ? 0.f : r_raw[qb];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[qb][kb] -= ru;
+        m_use[qb] = 0.f;
+      }
     }
 
     // Scores of the next tile (its K is resident) -- independent of the
@@ -205,27 +248,31 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     // B operand of O^T += V^T P^T.  For fp16 the row sum l adds the same
     // rounded probabilities that weight V, pairwise in FP32 (v_dot2 with
     // ones); bf16 keeps only 8 bits, so there l sums the FP32 values.
-    u32x4 pf[BN / 16];
+    u32x4 pf[QB][BN / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c2, -m_use));
-    float lsum = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int t = 0; t < BN / 16; ++t) {
-      pf[t] = pack8<T>(s[t >> 1], (t & 1) * 8);
-      if constexpr (T::id == Fp16::id) {
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(__builtin_fmaf(s[qb][kb][r], c2, -m_use[qb]));
+      float lsum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lsum = add_pair<T>(pf[t][e], lsum);
-      } else {
+      for (int t = 0; t < BN / 16; ++t) {
+        pf[qb][t] = pack8<T>(s[qb][t >> 1], (t & 1) * 8);
+        if constexpr (T::id == Fp16::id) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lsum += s[t >> 1][(t & 1) * 8 + e];
+          for (int e = 0; e < 4; ++e) lsum = add_pair<T>(pf[qb][t][e], lsum);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lsum += s[qb][t >> 1][(t & 1) * 8 + e];
+        }
       }
+      l_run[qb] += lsum;
     }
-    l_run += lsum;
 
     // O^T += V^T P^T, 16 keys per step: step t uses keys 16t .. 16t+15, which
     // are accumulator registers 8*(t%2) .. +7 of block t/2 (see acc_row).
+    // Each V^T fragment feeds the QB query blocks.
     const char* __restrict__ Vl = (const char*)Vcur;
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
@@ -235,13 +282,15 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         const int r0 = 16 * t + v_row0;
         const u32x2 lo = lds_read_tr16(Vl + v_chunk<RC>(r0, col >> 3) * 16 + (col & 7) * 2);
         const u32x2 hi = lds_read_tr16(Vl + v_chunk<RC>(r0 + 4, col >> 3) * 16 + (col & 7) * 2);
-        oacc[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[t], oacc[db]);
+        const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<T>(vf, pf[qb][t], oacc[qb][db]);
       }
     }
   };
 
   // Prologue: K and V of tile 0, K of tile 1, scores of tile 0.
-  f32x16 sA[2], sB[2];
+  f32x16 sA[QB][2], sB[QB][2];
   load_k(0, lds_k0);
   load_v(0, lds_v0);
   if (n_kt > 1) load_k(1, lds_k1);
@@ -254,35 +303,39 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   }
 
   if (!active) return;
-  const float l_tot = xhalf_sum(l_run);
-  const float inv = 1.f / l_tot;
-  uint16_t* Orow = a.o + head + (int64_t)my_q * D;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int my_q = q0w + 32 * qb + ql;
+    const float l_tot = xhalf_sum(l_run[qb]);
+    const float inv = 1.f / l_tot;
+    uint16_t* Orow = a.o + head + (int64_t)my_q * D;
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      u32x2 w;
-      w[0] = pack2<T>(oacc[db][rq * 4 + 0] * inv, oacc[db][rq * 4 + 1] * inv);
-      w[1] = pack2<T>(oacc[db][rq * 4 + 2] * inv, oacc[db][rq * 4 + 3] * inv);
-      *(u32x2*)(Orow + db * 32 + rq * 8 + g * 4) = w;
-    }
-  if (g == 0) a.lse[(int64_t)bh * N + my_q] = (r_raw * c2 + __log2f(l_tot)) * kLn2;
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        u32x2 w;
+        w[0] = pack2<T>(oacc[qb][db][rq * 4 + 0] * inv, oacc[qb][db][rq * 4 + 1] * inv);
+        w[1] = pack2<T>(oacc[qb][db][rq * 4 + 2] * inv, oacc[qb][db][rq * 4 + 3] * inv);
+        *(u32x2*)(Orow + db * 32 + rq * 8 + g * 4) = w;
+      }
+    if (g == 0) a.lse[(int64_t)bh * N + my_q] = (r_raw[qb] * c2 + __log2f(l_tot)) * kLn2;
+  }
 }
 
-template <int D, bool CAUSAL, class T>
-hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+template <int D, int QB, bool CAUSAL, class T>
+hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
+  constexpr int BM = FwdShape<QB>::BM;
+  a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, T>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int fwd_block_m() { return kFwdBM; }
-
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_FWD_CASE(DD, CC, TT) \
-  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_t<DD, CC, TT>(a, stream);
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_t<DD, kFwdQB, CC, TT>(a, stream);
   FA_FWD_CASE(64, false, Fp16)
   FA_FWD_CASE(64, true, Fp16)
   FA_FWD_CASE(128, false, Fp16)

@@ -14,7 +14,7 @@ struct FwdArgs {
   float* lse;
   int64_t N;
   int BH;          // B * H
-  int n_qtiles;    // ceil(N / fwd_block_m())
+  int n_qtiles;    // ceil(N / queries per workgroup), filled in by the launcher
   float scale_log2;  // scale * log2(e)
 };
 
@@ -35,7 +35,6 @@ struct BwdArgs {
   float scale_log2;  // scale * log2(e)
 };
 
-int fwd_block_m();
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 
