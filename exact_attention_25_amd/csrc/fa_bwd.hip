@@ -17,6 +17,9 @@
 //     registers and are written once.
 //  3. dq_kernel: one workgroup per 128 queries, Q and dO resident, looping
 //     over key tiles of 64; dQ accumulates in registers and is written once.
+// The streamed tiles go HBM -> LDS directly into a double-buffered ring (one
+// barrier per tile) and stay row-major; the transposed operands (Q^T, dO^T,
+// K^T) come from ds_read_b64_tr_b16, so nothing is transposed in memory.
 // Splitting dQ into its own pass (instead of atomically adding partial dQ
 // from every key tile) costs a second recomputation of S and dP but makes the
 // result bitwise reproducible.
@@ -77,105 +80,72 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Tile staging helpers.  A 64-row x D-column tile of a [.., D] row-major
-// tensor is kept in LDS as swizzled 16-byte chunks, either row-major
-// ("rows", D/8 chunks per row) or transposed ("cols": D rows of 64 entries,
-// 8 chunks per row).
+// Tiles of 64 rows x D columns of a row-major [.., D] tensor are copied from
+// HBM straight into LDS (global_load_lds_dwordx4, 256 threads, D/32 copies
+// each) as 16-byte chunks in row-major order.  A tile that is read both by
+// rows and transposed uses the dual_chunk swizzle; a tile read only by rows
+// uses swz.  Copy i of wave w fills LDS chunks i*256 + 64w + lane; because
+// both swizzles depend only on the low four bits of the row index, the
+// per-lane source offset of copy i is copy 0's plus i*256 chunks.
 // ---------------------------------------------------------------------------
 constexpr int kTileRows = 64;
 
-// 128 threads stage one tile into BOTH layouts: thread t owns rows
-// 8*(t/16) .. +7 and columns (D/16)*(t%16) .. +D/16-1.
-template <int D>
-struct DualStager {
-  static constexpr int CW = D / 16;  // columns per thread: 4 or 8
-  uint32_t buf[8][CW / 2];
-  int cg, rg;
-  __device__ void init(int t) {
-    cg = t % 16;
-    rg = t / 16;
+template <int D, bool DUAL>
+__device__ __forceinline__ int tile_src_offset(int p) {
+  constexpr int RC = D / 8;
+  if constexpr (DUAL) {
+    const int r = p / RC;
+    return r * D + ((p % RC) ^ dual_xor<RC>(r)) * 8;
+  } else {
+    return swz(p) * 8;  // swz is its own inverse
   }
-  __device__ void load(const uint16_t* __restrict__ src) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint16_t* p = src + (int64_t)(rg * 8 + r) * D + cg * CW;
-      if constexpr (CW == 8) {
-        const u32x4 x = *(const u32x4*)p;
-        buf[r][0] = x[0];
-        buf[r][1] = x[1];
-        buf[r][2] = x[2];
-        buf[r][3] = x[3];
-      } else {
-        const u32x2 x = *(const u32x2*)p;
-        buf[r][0] = x[0];
-        buf[r][1] = x[1];
-      }
-    }
-  }
-  __device__ void store(u32x4* lds_rows, u32x4* lds_cols) const {
-    constexpr int RCH = D / 8;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = rg * 8 + r;
-      if constexpr (CW == 8) {
-        lds_rows[swz(row * RCH + cg)] = u32x4{buf[r][0], buf[r][1], buf[r][2], buf[r][3]};
-      } else {
-        u32x2* dst = (u32x2*)&lds_rows[swz(row * RCH + (cg >> 1))];
-        dst[cg & 1] = u32x2{buf[r][0], buf[r][1]};
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < CW; ++j) {
-      u32x4 w;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t lo = buf[2 * p][j >> 1], hi = buf[2 * p + 1][j >> 1];
-        w[p] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      lds_cols[swz((cg * CW + j) * (kTileRows / 8) + rg)] = w;
-    }
-  }
-};
+}
 
-// 128 threads stage one tile row-major only, in 16-byte chunks.
 template <int D>
-struct RowStager {
-  static constexpr int PER = kTileRows * (D / 8) / 128;
-  u32x4 buf[PER];
-  int t;
-  __device__ void init(int t_) { t = t_; }
-  __device__ void load(const uint16_t* __restrict__ src) {
+__device__ __forceinline__ void copy_tile(const uint16_t* __restrict__ src, int src0, u32x4* dst, int wave) {
+  constexpr int LPT = kTileRows * (D / 8) / kThreads;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) buf[i] = *(const u32x4*)(src + (t + i * 128) * 8);
-  }
-  __device__ void store(u32x4* lds_rows) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) lds_rows[swz(t + i * 128)] = buf[i];
-  }
-};
+  for (int i = 0; i < LPT; ++i) copy16_to_lds(src + src0 + i * kThreads * 8, dst + i * kThreads + wave * 64);
+}
+
+// Transposed operand read from a dual-swizzled tile: rows r..r+3 (r = the
+// lane's row for this 16-lane group), column col (see lds_read_tr16).
+template <int RC>
+__device__ __forceinline__ int tr_offset(int r, int col) {
+  return dual_chunk<RC>(r, col >> 3) * 16 + (col & 7) * 2;
+}
 
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup = 128 keys of one head; wave w owns keys k0w .. k0w+31.
+// K and V rows stay in VGPRs as B operands; tiles of 64 queries of Q and dO
+// (plus their LSE and Delta) stream through a double-buffered LDS ring.
+//   S    = Q K^T        (A = Q rows,  B = K^T)        queries x keys
+//   dP   = dO V^T       (A = dO rows, B = V^T)
+//   P    = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - Delta)
+//   dV^T += dO^T P      (A = dO^T via transposed reads, B = P)
+//   dK^T += Q^T dS      (A = Q^T  via transposed reads, B = dS)
+// Query rows are read in perm23 order, so register r of lane-half g holds
+// query acc_row(r, g) of its 32-query block, and P / dS feed the next two
+// products straight from their accumulators.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, class T>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = kTileRows;
-  constexpr int RCH = D / 8, TCH = BQ / 8;
-  __shared__ u32x4 lds_q[BQ * RCH];
-  __shared__ u32x4 lds_qt[D * TCH];
-  __shared__ u32x4 lds_do[BQ * RCH];
-  __shared__ u32x4 lds_dot[D * TCH];
-  __shared__ __attribute__((aligned(16))) float lds_lse[BQ];
-  __shared__ __attribute__((aligned(16))) float lds_dl[BQ];
+  constexpr int RC = D / 8, TC = BQ * RC;
+  __shared__ u32x4 lq0[TC], lq1[TC], lg0[TC], lg1[TC];
+  __shared__ __attribute__((aligned(16))) float ll0[BQ], ll1[BQ], ld0[BQ], ld1[BQ];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int64_t N = a.N;
   const int bh = blockIdx.x % a.BH;
   const int kt = blockIdx.x / a.BH;  // key tiles heaviest (lowest) first
   const int64_t head = (int64_t)bh * N * D;
   const int64_t rowbase = (int64_t)bh * N;
+  const uint16_t* __restrict__ Qh = a.q + head;
+  const uint16_t* __restrict__ Gh = a.dout + head;
 
   const int k0w = kt * BK + wave * 32;
   const bool active = k0w < N;
@@ -196,55 +166,60 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  const bool is_q_stager = tid < 128;  // waves 0-1 stage Q, waves 2-3 stage dO
-  DualStager<D> st;
-  st.init(tid & 127);
-  const uint16_t* stage_src = (is_q_stager ? a.q : a.dout) + head;
-  u32x4* lds_rows = is_q_stager ? lds_q : lds_do;
-  u32x4* lds_cols = is_q_stager ? lds_qt : lds_dot;
-  float lse_next = 0.f, dl_next = 0.f;
+  // LDS byte offsets (see fwd): row reads of query row qb*32 + perm23(l32),
+  // chunk 2c + g; transposed reads of rows qb*32 + 16*t2 + 8g + j/4 (+4),
+  // columns 32db + 16(q%2) + 4(j%4).  Whole 16-row steps are immediates.
+  int roff[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) roff[c] = dual_chunk<RC>(perm23(l32), 2 * c + g) * 16;
+  const int vj = lane & 15, vq = lane >> 4;
+  const int t_row0 = 8 * g + (vj >> 2);
+  const int t_col = 16 * (vq & 1) + 4 * (vj & 3);
+  int toff[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) toff[db][h] = tr_offset<RC>(t_row0 + 4 * h, db * 32 + t_col);
+  constexpr int ROW16 = 16 * RC * 16;  // bytes of 16 rows
 
+  const int src0 = tile_src_offset<D, true>(wave * 64 + lane);
   const int n_qt = (int)(N / BQ);
   const int qt_begin = CAUSAL ? (kt * BK) / BQ : 0;
   const float c2 = a.scale_log2;
 
-  auto load = [&](int qt) {
-    st.load(stage_src + (int64_t)qt * BQ * D);
+  // LSE (times log2 e) and Delta of the next tile travel through registers of
+  // threads 0..63 and are written to LDS at the end of a step.
+  float lse_n = 0.f, dl_n = 0.f;
+  auto fetch_rows = [&](int qt) {
     if (tid < BQ) {
-      lse_next = a.lse[rowbase + qt * BQ + tid] * kLog2e;
-      dl_next = a.delta[rowbase + qt * BQ + tid];
+      lse_n = a.lse[rowbase + (int64_t)qt * BQ + tid] * kLog2e;
+      dl_n = a.delta[rowbase + (int64_t)qt * BQ + tid];
+    }
+  };
+  auto put_rows = [&](float* ll, float* ld) {
+    if (tid < BQ) {
+      ll[tid] = lse_n;
+      ld[tid] = dl_n;
     }
   };
 
-  if (qt_begin < n_qt) load(qt_begin);
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
-    __syncthreads();
-    st.store(lds_rows, lds_cols);
-    if (tid < BQ) {
-      lds_lse[tid] = lse_next;
-      lds_dl[tid] = dl_next;
-    }
-    __syncthreads();
-    if (qt + 1 < n_qt) load(qt + 1);
-    if (!active) continue;
-
+  auto compute = [&](int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
+    const char* Qb = (const char*)Ql;
+    const char* Gb = (const char*)Gl;
     const int q0 = qt * BQ;
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int qb0 = q0 + qb * 32;
       if (CAUSAL && qb0 + 31 < k0w) continue;  // every query precedes every key
-      // S (queries x keys) and dP = dO V^T, query rows read in perm23 order.
       f32x16 s = f32x16{}, dp = f32x16{};
-      const int arow = qb * 32 + perm23(l32);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        s = mfma32<T>(lds_q[swz(arow * RCH + 2 * c + g)], kf[c], s);
-        dp = mfma32<T>(lds_do[swz(arow * RCH + 2 * c + g)], vf[c], dp);
+        s = mfma32<T>(*(const u32x4*)(Qb + qb * 2 * ROW16 + roff[c]), kf[c], s);
+        dp = mfma32<T>(*(const u32x4*)(Gb + qb * 2 * ROW16 + roff[c]), vf[c], dp);
       }
-      // P = exp2(S*scale*log2e - LSE*log2e); dS = P (dP - Delta).
       // Register r holds query qb*32 + acc_row(r, g): two runs of 8.
-      const f32x4* lse4 = (const f32x4*)lds_lse;
-      const f32x4* dl4 = (const f32x4*)lds_dl;
+      const f32x4* lse4 = (const f32x4*)ll;
+      const f32x4* dl4 = (const f32x4*)ld;
       float lse_r[16], dl_r[16];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -266,19 +241,46 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
         s[r] = p;
         dp[r] = p * (dp[r] - dl_r[r]);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries, 16 per step.
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const u32x4 pf = pack8<T>(s, t2 * 8);
         const u32x4 sf = pack8<T>(dp, t2 * 8);
-        const int ch = qb * 4 + t2 * 2 + g;
+        const int rows = (qb * 2 + t2) * ROW16;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dv[db] = mfma32<T>(lds_dot[swz((db * 32 + l32) * TCH + ch)], pf, dv[db]);
-          dk[db] = mfma32<T>(lds_qt[swz((db * 32 + l32) * TCH + ch)], sf, dk[db]);
+          const u32x2 glo = lds_read_tr16(Gb + rows + toff[db][0]);
+          const u32x2 ghi = lds_read_tr16(Gb + rows + toff[db][1]);
+          dv[db] = mfma32<T>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pf, dv[db]);
+          const u32x2 qlo = lds_read_tr16(Qb + rows + toff[db][0]);
+          const u32x2 qhi = lds_read_tr16(Qb + rows + toff[db][1]);
+          dk[db] = mfma32<T>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sf, dk[db]);
         }
       }
     }
+  };
+
+  auto step = [&](int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld, u32x4* Qn,
+                  u32x4* Gn, float* lln, float* ldn) {
+    wait_vmem();      // this wave's copies of tile qt have landed
+    __syncthreads();  // everyone's have (and the LSE/Delta rows); tile qt-1 is done
+    if (qt + 1 < n_qt) {
+      fetch_rows(qt + 1);  // first, so that storing them later need not wait for the tile copies
+      copy_tile<D>(Qh + (int64_t)(qt + 1) * BQ * D, src0, Qn, wave);
+      copy_tile<D>(Gh + (int64_t)(qt + 1) * BQ * D, src0, Gn, wave);
+    }
+    if (active) compute(qt, Ql, Gl, ll, ld);
+    if (qt + 1 < n_qt) put_rows(lln, ldn);
+  };
+
+  if (qt_begin < n_qt) {
+    copy_tile<D>(Qh + (int64_t)qt_begin * BQ * D, src0, lq0, wave);
+    copy_tile<D>(Gh + (int64_t)qt_begin * BQ * D, src0, lg0, wave);
+    fetch_rows(qt_begin);
+    put_rows(ll0, ld0);
+  }
+  for (int qt = qt_begin; qt < n_qt; qt += 2) {
+    step(qt, lq0, lg0, ll0, ld0, lq1, lg1, ll1, ld1);
+    if (qt + 1 < n_qt) step(qt + 1, lq1, lg1, ll1, ld1, lq0, lg0, ll0, ld0);
   }
 
   if (!active) return;
@@ -299,17 +301,22 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 128 queries of one head; wave w owns queries q0w .. q0w+31.
+// Q and dO rows stay in VGPRs as B operands; tiles of 64 keys of K and V
+// stream through a double-buffered LDS ring.
+//   S^T  = K Q^T        (A = K rows, B = Q^T)         keys x queries
+//   dP^T = V dO^T       (A = V rows, B = dO^T)
+//   P^T  = exp2(S^T*scale*log2e - LSE*log2e), dS^T = P^T (dP^T - Delta)
+//   dQ^T += K^T dS^T    (A = K^T via transposed reads, B = dS^T)
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, class T>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_kernel(BwdArgs a) {
   constexpr int BM = 128, BN = kTileRows;
-  constexpr int RCH = D / 8, TCH = BN / 8;
-  __shared__ u32x4 lds_k[BN * RCH];
-  __shared__ u32x4 lds_kt[D * TCH];
-  __shared__ u32x4 lds_v[BN * RCH];
+  constexpr int RC = D / 8, TC = BN * RC;
+  __shared__ u32x4 lk0[TC], lk1[TC], lv0[TC], lv1[TC];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, g = lane >> 5;
   const int64_t N = a.N;
   const int n_qtiles = (int)((N + BM - 1) / BM);
@@ -317,6 +324,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_kernel(BwdArgs a
   const int rank = blockIdx.x / a.BH;
   const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
   const int64_t head = (int64_t)bh * N * D;
+  const uint16_t* __restrict__ Kh = a.k + head;
+  const uint16_t* __restrict__ Vh = a.v + head;
 
   const int q0w = qt * BM + wave * 32;
   const bool active = q0w < N;
@@ -335,46 +344,45 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_kernel(BwdArgs a
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
 
-  const bool is_k_stager = tid < 128;  // waves 0-1 stage K (both layouts), 2-3 stage V
-  DualStager<D> kst;
-  RowStager<D> vst;
-  kst.init(tid & 127);
-  vst.init(tid & 127);
-  auto load = [&](int kt) {
-    const int64_t off = head + (int64_t)kt * BN * D;
-    if (is_k_stager)
-      kst.load(a.k + off);
-    else
-      vst.load(a.v + off);
-  };
+  // LDS byte offsets: K rows (dual swizzle) and V rows (swz) of key
+  // kb*32 + perm23(ql), chunk 2c + g; transposed K reads of rows
+  // 16t + 8g + j/4 (+4), columns 32db + 16(q%2) + 4(j%4).
+  const int krow = perm23(ql);
+  int koff[D / 16], voff[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    koff[c] = dual_chunk<RC>(krow, 2 * c + g) * 16;
+    voff[c] = swz(krow * RC + 2 * c + g) * 16;
+  }
+  const int vj = lane & 15, vq = lane >> 4;
+  const int t_row0 = 8 * g + (vj >> 2);
+  const int t_col = 16 * (vq & 1) + 4 * (vj & 3);
+  int toff[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) toff[db][h] = tr_offset<RC>(t_row0 + 4 * h, db * 32 + t_col);
+  constexpr int ROW16 = 16 * RC * 16;
 
+  const int ksrc0 = tile_src_offset<D, true>(wave * 64 + lane);
+  const int vsrc0 = tile_src_offset<D, false>(wave * 64 + lane);
   const int n_kt_all = (int)(N / BN);
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
   const float c2 = a.scale_log2;
 
-  load(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    if (is_k_stager)
-      kst.store(lds_k, lds_kt);
-    else
-      vst.store(lds_v);
-    __syncthreads();
-    if (kt + 1 < n_kt) load(kt + 1);
-
+  auto compute = [&](int kt, const u32x4* Kl, const u32x4* Vl) {
+    const char* Kb = (const char*)Kl;
+    const char* Vb = (const char*)Vl;
     const int k0 = kt * BN;
-    if (!active || (CAUSAL && k0 > q0w + 31)) continue;
-
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
-      const int krow = kb * 32 + perm23(ql);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        s[kb] = mfma32<T>(lds_k[swz(krow * RCH + 2 * c + g)], qf[c], s[kb]);
-        dp[kb] = mfma32<T>(lds_v[swz(krow * RCH + 2 * c + g)], gf[c], dp[kb]);
+        s[kb] = mfma32<T>(*(const u32x4*)(Kb + kb * 2 * ROW16 + koff[c]), qf[c], s[kb]);
+        dp[kb] = mfma32<T>(*(const u32x4*)(Vb + kb * 2 * ROW16 + voff[c]), gf[c], dp[kb]);
       }
     }
     const bool diag = CAUSAL && k0 + BN - 1 > q0w;
@@ -391,9 +399,30 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_kernel(BwdArgs a
     for (int t = 0; t < BN / 16; ++t) {
       const u32x4 sf = pack8<T>(dp[t >> 1], (t & 1) * 8);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        dq[db] = mfma32<T>(lds_kt[swz((db * 32 + ql) * TCH + 2 * t + g)], sf, dq[db]);
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x2 lo = lds_read_tr16(Kb + t * ROW16 + toff[db][0]);
+        const u32x2 hi = lds_read_tr16(Kb + t * ROW16 + toff[db][1]);
+        dq[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf, dq[db]);
+      }
     }
+  };
+
+  auto step = [&](int kt, const u32x4* Kl, const u32x4* Vl, u32x4* Kn, u32x4* Vn) {
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < n_kt) {
+      copy_tile<D>(Kh + (int64_t)(kt + 1) * BN * D, ksrc0, Kn, wave);
+      copy_tile<D>(Vh + (int64_t)(kt + 1) * BN * D, vsrc0, Vn, wave);
+    }
+    if (!active || (CAUSAL && kt * BN > q0w + 31)) return;
+    compute(kt, Kl, Vl);
+  };
+
+  copy_tile<D>(Kh, ksrc0, lk0, wave);
+  copy_tile<D>(Vh, vsrc0, lv0, wave);
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    step(kt, lk0, lv0, lk1, lv1);
+    if (kt + 1 < n_kt) step(kt + 1, lk1, lv1, lk0, lv0);
   }
 
   if (!active) return;

@@ -102,6 +102,21 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& s, int lo) {
 // position is XORed with the line index.
 __device__ __forceinline__ int swz(int chunk) { return chunk ^ ((chunk >> 4) & 15); }
 
+// Chunk swizzle for a tile (RC 16-byte chunks per row) that is read both by
+// rows (16 lanes, 16 different rows, same logical chunk, ds_read_b128) and
+// transposed (ds_read_b64_tr_b16: 4 consecutive rows x 2 adjacent chunks per
+// 16-lane group).  The XOR value takes 16 (RC = 16) or, per row parity, 8
+// distinct values over 16 consecutive rows and 4 distinct values with equal
+// low bit over 4 aligned rows, so both patterns hit distinct banks.
+template <int RC>
+__device__ __forceinline__ int dual_xor(int r) {
+  return RC == 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int RC>
+__device__ __forceinline__ int dual_chunk(int r, int c) {
+  return r * RC + (c ^ dual_xor<RC>(r));
+}
+
 // Swap bits 2 and 3 of a row index inside a 32-row MFMA block.  Reading
 // operand rows in this order makes accumulator register r of lane-half g
 // hold row 16*(r/8) + 8*g + (r%8) -- eight consecutive rows per half -- so a
