@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
 //   dQ^T += K^T dS^T    (A = K^T via transposed reads, B = dS^T)
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, class T>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   constexpr int BM = 128, BN = kTileRows;
   constexpr int RC = D / 8, TC = BN * RC;
   __shared__ u32x4 lk0[TC], lk1[TC], lv0[TC], lv1[TC];
