@@ -51,6 +51,11 @@ def load_library():
     lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                            ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
     lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_str.argtypes = [ctypes.c_int]
@@ -72,6 +77,16 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype,
            workspace, workspace_bytes, stream):
     return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, int(causal),
                                  float(scale), int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, num_splits, workspace,
+                   workspace_bytes, stream):
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, D, int(causal), float(scale), int(dtype),
+                                         int(num_splits), workspace, workspace_bytes, stream)
+
+
+def fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits):
+    return int(load_library().fa_fwd_splitkv_workspace_bytes(B, H, N, D, int(causal), int(dtype), int(num_splits)))
 
 
 def bwd_workspace_bytes(B, H, N, D, causal, dtype):
@@ -129,6 +144,32 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
                 B, H, N, D, causal, scale, _dtype_code(q), _stream_handle(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, num_splits, causal=False, scale=None, out=None, lse=None, workspace=None):
+    """fa_fwd_splitkv: the forward with keys split into num_splits ranges and
+    the partial states merged.  Returns (o, lse) like fwd."""
+    import torch
+    B, H, N, D = q.shape
+    _check({"q": q, "k": k, "v": v}, q.shape, q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check({"out": out}, q.shape, q.dtype, q.device)
+    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
+    need = fwd_splitkv_workspace_bytes(B, H, N, D, causal, code, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D,
+                        causal, scale, code, num_splits, workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv")
     return out, lse
 
 

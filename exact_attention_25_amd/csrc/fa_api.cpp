@@ -12,6 +12,9 @@
 namespace {
 
 constexpr int64_t kMaxWorkgroups = (int64_t(1) << 31) - 1;
+constexpr int kMaxSplits = 64;
+
+size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -63,7 +66,49 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.BH = static_cast<int>(B * H);
   a.n_qtiles = 0;  // set by the launcher from its tile shape
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.n_splits = 1;
+  a.part_lse = nullptr;
+  a.part_o = nullptr;
   hipError_t e = fa::launch_fwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                                      int num_splits) {
+  if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK) return 0;
+  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
+  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
+  return align256(rows * sizeof(float)) + align256(rows * static_cast<size_t>(D) * sizeof(float));
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if (B * H * (N / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.N = N;
+  a.BH = static_cast<int>(B * H);
+  a.n_qtiles = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.n_splits = num_splits;
+  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
+  a.part_lse = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
+  hipError_t e =
+      fa::launch_fwd_splitkv(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

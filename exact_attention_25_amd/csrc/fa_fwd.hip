@@ -61,7 +61,10 @@ struct FwdShape {
   static constexpr int BM = 32 * QB * (kFwdThreads / 64);  // queries per workgroup
 };
 
-template <int D, int QB, bool CAUSAL, class T>
+// SPLIT: the workgroup covers only key tiles [kt_begin, kt_end) of its split
+// and writes FP32 partial states (O normalised within the range, and the
+// range's LSE) for merge_kernel instead of the final O and LSE.
+template <int D, int QB, bool CAUSAL, class T, bool SPLIT>
 __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdArgs a) {
   constexpr int BM = FwdShape<QB>::BM, BN = kFwdBN, NT = kFwdThreads;
   constexpr int RC = D / 8;              // 16-byte chunks per row
@@ -81,7 +84,8 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
 
   const int64_t N = a.N;
   const int bh = blockIdx.x % a.BH;
-  const int rank = blockIdx.x / a.BH;
+  const int split = SPLIT ? (blockIdx.x / a.BH) % a.n_splits : 0;
+  const int rank = SPLIT ? blockIdx.x / (a.BH * a.n_splits) : blockIdx.x / a.BH;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - rank) : rank;
   const int64_t head = (int64_t)bh * N * D;
   const uint16_t* __restrict__ Qh = a.q + head;
@@ -113,6 +117,9 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
 
   const int n_kt_all = (int)(N / BN);
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
+  // Key tiles of this workgroup: all visible ones, or this split's share.
+  const int kt_begin = SPLIT ? (int)(((int64_t)split * n_kt_all) / a.n_splits) : 0;
+  const int kt_end = SPLIT ? min(n_kt, (int)(((int64_t)(split + 1) * n_kt_all) / a.n_splits)) : n_kt;
 
   // Direct copies: copy i of wave w fills LDS chunks i*NT + 64w + lane.  The
   // per-lane source offsets (elements within a tile) differ between copies
@@ -168,8 +175,8 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
                   u32x4* vdst, f32x16 (&s)[QB][2], f32x16 (&s_nxt)[QB][2]) {
     wait_vmem();      // K of tile kt+1 and V of tile kt have landed (this wave's part)
     __syncthreads();  // ... everyone's part; everyone is done with tile kt-1
-    if (kt + 2 < n_kt) load_k(kt + 2, kdst);
-    if (kt + 1 < n_kt) load_v(kt + 1, vdst);
+    if (kt + 2 < kt_end) load_k(kt + 2, kdst);
+    if (kt + 1 < kt_end) load_v(kt + 1, vdst);
 
     const int k0 = kt * BN;
     if (!active || (CAUSAL && k0 > q0w + WQ - 1)) return;  // nothing visible
@@ -289,20 +296,47 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     }
   };
 
-  // Prologue: K and V of tile 0, K of tile 1, scores of tile 0.
+  // Prologue: K and V of the first tile, K of the second, scores of the first.
   f32x16 sA[QB][2], sB[QB][2];
-  load_k(0, lds_k0);
-  load_v(0, lds_v0);
-  if (n_kt > 1) load_k(1, lds_k1);
-  wait_vmem();
-  __syncthreads();
-  if (active) scores(lds_k0, sA);
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    step(kt, lds_k1, lds_v0, lds_k0, lds_v1, sA, sB);
-    if (kt + 1 < n_kt) step(kt + 1, lds_k0, lds_v1, lds_k1, lds_v0, sB, sA);
+  if (kt_begin < kt_end) {  // workgroup-uniform
+    load_k(kt_begin, lds_k0);
+    load_v(kt_begin, lds_v0);
+    if (kt_begin + 1 < kt_end) load_k(kt_begin + 1, lds_k1);
+    wait_vmem();
+    __syncthreads();
+    if (active) scores(lds_k0, sA);
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
+      step(kt, lds_k1, lds_v0, lds_k0, lds_v1, sA, sB);
+      if (kt + 1 < kt_end) step(kt + 1, lds_k0, lds_v1, lds_k1, lds_v0, sB, sA);
+    }
   }
 
   if (!active) return;
+  if constexpr (SPLIT) {
+    // Partial state of this split: O normalised within the split, FP32, and
+    // the split's natural-log LSE; a row that saw no key in the split gets
+    // O = 0 and LSE = -inf, which the merge weights by zero.
+    const int64_t rows = (int64_t)a.BH * N;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int my_q = q0w + 32 * qb + ql;
+      const float l_tot = xhalf_sum(l_run[qb]);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const int64_t row = (int64_t)bh * N + my_q;
+      float* Orow = a.part_o + ((int64_t)split * rows + row) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *(f32x4*)(Orow + db * 32 + rq * 8 + g * 4) =
+              f32x4{oacc[qb][db][rq * 4 + 0] * inv, oacc[qb][db][rq * 4 + 1] * inv,
+                    oacc[qb][db][rq * 4 + 2] * inv, oacc[qb][db][rq * 4 + 3] * inv};
+      if (g == 0)
+        a.part_lse[(int64_t)split * rows + row] =
+            l_tot > 0.f ? (r_raw[qb] * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int my_q = q0w + 32 * qb + ql;
@@ -322,12 +356,60 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   }
 }
 
+// Merge of split-K/V partial states, one row per D/4 lanes ("CUDA
+// FlashAttention ...", §7: split along K, each part yields local (m, l, o),
+// combined with the same merge formula).  With LSE_s the natural-log
+// log-sum-exp of split s and O_s its normalised output,
+//   LSE = m + ln sum_s exp(LSE_s - m),  O = sum_s exp(LSE_s - LSE) O_s,
+// where m = max_s LSE_s; splits with LSE_s = -inf carry weight 0.
+template <int D, class T>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_lse,
+                                                    const float* __restrict__ part_o, uint16_t* __restrict__ o,
+                                                    float* __restrict__ lse, int64_t rows, int n_splits) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int sp = 0; sp < n_splits; ++sp) m = fmaxf(m, part_lse[(int64_t)sp * rows + row]);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const float ls = part_lse[(int64_t)sp * rows + row];
+      const float w = ls == -INFINITY ? 0.f : fast_exp2((ls - m) * kLog2e);
+      const f32x4 x = *(const f32x4*)(part_o + ((int64_t)sp * rows + row) * D + c * 4);
+      acc += w * x;
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  *(u32x2*)(o + row * D + c * 4) = u32x2{pack2<T>(acc[0] * inv, acc[1] * inv), pack2<T>(acc[2] * inv, acc[3] * inv)};
+  if (c == 0) lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
 template <int D, int QB, bool CAUSAL, class T>
 hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int QB, bool CAUSAL, class T>
+hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
+  constexpr int BM = FwdShape<QB>::BM;
+  a.n_qtiles = (int)((a.N + BM - 1) / BM);
+  const int64_t n_wg = (int64_t)a.BH * a.n_qtiles * a.n_splits;
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.BH * a.N;
+  constexpr int rpb = 256 / (D / 4);
+  hipLaunchKernelGGL((merge_kernel<D, T>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream,
+                     a.part_lse, a.part_o, a.o, a.lse, rows, a.n_splits);
   return hipGetLastError();
 }
 
@@ -336,6 +418,21 @@ hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_FWD_CASE(DD, CC, TT) \
   if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_t<DD, kFwdQB, CC, TT>(a, stream);
+  FA_FWD_CASE(64, false, Fp16)
+  FA_FWD_CASE(64, true, Fp16)
+  FA_FWD_CASE(128, false, Fp16)
+  FA_FWD_CASE(128, true, Fp16)
+  FA_FWD_CASE(64, false, Bf16)
+  FA_FWD_CASE(64, true, Bf16)
+  FA_FWD_CASE(128, false, Bf16)
+  FA_FWD_CASE(128, true, Bf16)
+#undef FA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_FWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT>(a, stream);
   FA_FWD_CASE(64, false, Fp16)
   FA_FWD_CASE(64, true, Fp16)
   FA_FWD_CASE(128, false, Fp16)

@@ -16,6 +16,11 @@ struct FwdArgs {
   int BH;          // B * H
   int n_qtiles;    // ceil(N / queries per workgroup), filled in by the launcher
   float scale_log2;  // scale * log2(e)
+  // Split-K/V mode only: number of key ranges and the FP32 partial states,
+  // part_lse [n_splits][B*H*N] and part_o [n_splits][B*H*N][D].
+  int n_splits;
+  float* part_lse;
+  float* part_o;
 };
 
 struct BwdArgs {
@@ -36,6 +41,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 
 }  // namespace fa

@@ -81,6 +81,39 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int causal, float scale, int dtype, void* stream);
 
 /*
+ * fa_fwd_splitkv_workspace_bytes -- bytes of device workspace fa_fwd_splitkv
+ * needs for num_splits partial states: an FP32 LSE and an FP32 D-vector per
+ * query row and split, i.e. num_splits*B*H*N*(D+1)*4 (each part rounded up
+ * to 256).  Returns 0 for arguments fa_fwd_splitkv would reject.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
+                                      int causal, int dtype, int num_splits);
+
+/*
+ * fa_fwd_splitkv -- the same result as fa_fwd, with the keys split into
+ * num_splits contiguous ranges of whole 64-key tiles ("CUDA FlashAttention
+ * ...", §7: for long N and small B*H, split along K; every part yields a
+ * local (m, l, o) and the parts are combined with the merge formula of §4).
+ *   Pass 1: one workgroup per (query tile, split) writes, for each query row,
+ *           the split's LSE_s and its output O_s normalised within the split
+ *           (FP32, in `workspace`); a row with no visible key in the split
+ *           gets LSE_s = -inf.
+ *   Pass 2: per row, LSE = m + ln sum_s exp(LSE_s - m) with m = max_s LSE_s,
+ *           and O = sum_s exp(LSE_s - LSE) O_s, rounded to `dtype` (RNE).
+ *   num_splits : 1 .. 64 (more splits than key tiles leaves some empty).
+ *   workspace  : caller-owned device memory of at least
+ *                fa_fwd_splitkv_workspace_bytes(...) bytes, 16-byte aligned;
+ *                contents on entry ignored, on return unspecified.
+ *   Other arguments, layouts and errors as for fa_fwd; additionally
+ *   FA_ERR_WORKSPACE for a missing or short workspace and
+ *   FA_ERR_UNSUPPORTED for num_splits outside 1 .. 64.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t N, int64_t D,
+                   int causal, float scale, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one FP32
  * value per query row for Delta_i = rowsum(dO_i * O_i), i.e. 4*B*H*N, rounded
  * up to 256.  Returns 0 for arguments fa_bwd would reject.

@@ -35,6 +35,8 @@ from .attention import (  # noqa: F401
     attention_probs,
     online_forward,
     merge_states,
+    attention_partial,
+    merge_lse,
     brute_force_forward,
     causal_tile_count,
 )

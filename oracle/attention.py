@@ -243,6 +243,53 @@ def online_forward(q, k, v, causal, scale, block_q=64, block_k=64,
     return o_out, lse_out, {"tiles": tiles, "trace": trace}
 
 
+def attention_partial(q, k, v, causal, scale, key_lo, key_hi):
+    """Attention of every query over the keys key_lo .. key_hi-1 only.
+
+    Returns (O_s, LSE_s): O_s [B,H,N,D] is the output normalised over that key
+    range, LSE_s [B,H,N] the natural-log log-sum-exp of the masked scores in
+    the range; a row that sees no key of the range (causal, i < key_lo) gets
+    O_s = 0 and LSE_s = -inf.  This is the local state a key split produces
+    before merging ("CUDA FlashAttention ...", §7).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check4(q, k, v)
+    B, H, N, D = q.shape
+    o = np.zeros((B, H, N, D))
+    lse = np.full((B, H, N), NEG_INF)
+    cols = np.arange(key_lo, key_hi)
+    if key_hi <= key_lo:
+        return o, lse
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h, key_lo:key_hi].T)
+            if causal:
+                s = np.where(cols[None, :] > np.arange(N)[:, None], NEG_INF, s)
+            m = s.max(axis=1)
+            seen = np.isfinite(m)
+            mm = np.where(seen, m, 0.0)
+            e = np.exp(s - mm[:, None])
+            l = e.sum(axis=1)
+            o[b, h, seen] = (e[seen] / l[seen, None]) @ v[b, h, key_lo:key_hi]
+            lse[b, h, seen] = m[seen] + np.log(l[seen])
+    return o, lse
+
+
+def merge_lse(lses, outs):
+    """Combine per-split (LSE_s, O_s) pairs (O_s normalised within split s):
+    LSE = m + ln sum_s exp(LSE_s - m), O = sum_s exp(LSE_s - LSE) O_s, with
+    m = max_s LSE_s; splits with LSE_s = -inf weigh zero.  This is the merge
+    of [FA-CUDA] §4 written for normalised partial outputs."""
+    lses = [_f64(x) for x in lses]
+    m = np.max(np.stack(lses), axis=0)
+    mm = np.where(np.isfinite(m), m, 0.0)
+    ws = [np.where(np.isneginf(x), 0.0, np.exp(np.where(np.isneginf(x), 0.0, x) - mm)) for x in lses]
+    tot = sum(ws)
+    lse = np.where(tot > 0, mm + np.log(np.where(tot > 0, tot, 1.0)), NEG_INF)
+    o = sum(w[..., None] * _f64(x) for w, x in zip(ws, outs)) / np.where(tot > 0, tot, 1.0)[..., None]
+    return o, lse
+
+
 def causal_tile_count(n, block):
     """Number of (query tile, key tile) pairs a causal tiled pass computes
     when tiles wholly above the diagonal are skipped ([FA-WHY] §4.5),

@@ -24,7 +24,8 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_splitkv",
+                                    "fa_fwd_splitkv_workspace_bytes", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -90,3 +91,27 @@ def test_workspace_bytes():
     assert fb.bwd_workspace_bytes(2, 3, 128, 64, 1, 0) == 2 * 3 * 128 * 4
     assert fb.bwd_workspace_bytes(1, 1, 64, 128, 0, 1) == 256
     assert fb.bwd_workspace_bytes(1, 1, 100, 64, 0, 0) == 0
+
+
+def split(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=256, D=128, causal=1, scale=0.1, dtype=1, s=4,
+             ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return fb.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"],
+                             a["causal"], a["scale"], a["dtype"], a["s"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(s=0), 3), (dict(s=65), 3), (dict(N=200), 3),
+    (dict(ws=None), 5), (dict(wsb=1000), 5), (dict(ws=P + 8), 4), (dict(v=P + 2), 4), (dict(B=0), 2),
+])
+def test_splitkv_rejects(kw, code):
+    assert split(**kw) == code
+
+
+def test_splitkv_workspace_bytes():
+    rows = 2 * 3 * 128 * 4
+    assert fb.fwd_splitkv_workspace_bytes(2, 3, 128, 64, 1, 0, 4) == rows * 4 + rows * 64 * 4
+    assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 1) == 256 + 64 * 128 * 4
+    assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 0) == 0
+    assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 65) == 0

@@ -307,3 +307,30 @@ def test_selected_rows_match_brute_force(causal):
     ob, lb = brute_force_forward(q.tolist(), k.tolist(), v.tolist(), causal, 0.8)
     assert np.abs(o[0, 0] - np.array(ob)[rows]).max() < 1e-14
     assert np.abs(lse[0, 0] - np.array(lb)[rows]).max() < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Key splits and their merge ("CUDA FlashAttention ...", §7)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cuts", [(0, 40), (0, 13, 27, 40), (0, 1, 39, 40), (0, 20, 20, 40)])
+def test_merged_key_splits_equal_full_attention(causal, cuts):
+    from oracle import attention_partial, merge_lse
+    q, k, v = _rand(100, 1, 2, 40, 8), _rand(101, 1, 2, 40, 8), _rand(102, 1, 2, 40, 8)
+    parts = [attention_partial(q, k, v, causal, 0.3, lo, hi) for lo, hi in zip(cuts[:-1], cuts[1:])]
+    o, lse = merge_lse([p[1] for p in parts], [p[0] for p in parts])
+    o_ref, lse_ref = attention_forward(q, k, v, causal, 0.3)
+    assert np.abs(o - o_ref).max() < 1e-13
+    assert np.abs(lse - lse_ref).max() < 1e-13
+
+
+def test_partial_of_unseen_keys_is_empty():
+    from oracle import attention_partial
+    q, k, v = _rand(103, 1, 1, 16, 4), _rand(104, 1, 1, 16, 4), _rand(105, 1, 1, 16, 4)
+    o, lse = attention_partial(q, k, v, True, 0.5, 8, 16)
+    assert np.all(np.isneginf(lse[0, 0, :8])) and np.all(o[0, 0, :8] == 0)
+    assert np.all(np.isfinite(lse[0, 0, 8:]))
+    # a single key: the output is that key's value row
+    o1, lse1 = attention_partial(q, k, v, False, 0.5, 3, 4)
+    assert np.abs(o1[0, 0] - v[0, 0, 3]).max() < 1e-15
+    assert np.abs(lse1[0, 0] - 0.5 * (q[0, 0] @ k[0, 0, 3])).max() < 1e-14
