@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--mode", default="bench", choices=["bench", "copy", "fwd-only", "bwd-only"])
+    p.add_argument("--splits", type=int, default=0,
+                   help="time fa_fwd_splitkv with this many key splits (split pass + merge) instead of fa_fwd")
     return p.parse_args()
 
 
@@ -151,8 +153,15 @@ def main():
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def run_fwd():
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    if args.splits > 0:
+        split_ws = torch.empty(max(256, fa.fwd_splitkv_workspace_bytes(
+            w.B, w.H, w.N, w.D, w.causal, 0 if w.dtype == "fp16" else 1, args.splits)), dtype=torch.uint8, device=dev)
+
+        def run_fwd():
+            fa.fwd_splitkv(q, k, v, args.splits, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=split_ws)
+    else:
+        def run_fwd():
+            fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
     ws = torch.empty(max(256, fa.bwd_workspace_bytes(w.B, w.H, w.N, w.D, w.causal, 0 if w.dtype == "fp16" else 1)),
                      dtype=torch.uint8, device=dev)
@@ -187,7 +196,7 @@ def main():
     bwd_ms = timed(run_bwd, max(1, args.steps // 2), max(1, args.warmup // 2))
     bwd_tflops = w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
 
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name) if args.splits == 0 else None
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -208,7 +217,8 @@ def main():
         "pct_mfma_peak": round(100 * tflops / PEAK_TFLOPS_FP16, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "fwd_kernel<%d,%s>" % (w.D, "causal" if w.causal else "full"),
+            "kernel": ("fwd_kernel<%d,%s> split x%d + merge_kernel" % (w.D, "causal" if w.causal else "full", args.splits)
+                       if args.splits > 0 else "fwd_kernel<%d,%s>" % (w.D, "causal" if w.causal else "full")),
             "achieved": round(tflops, 2),
             "peak": PEAK_TFLOPS_FP16,
             "unit": "TFLOP/s",
