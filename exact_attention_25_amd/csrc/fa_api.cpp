@@ -12,6 +12,7 @@
 namespace {
 
 constexpr int64_t kMaxWorkgroups = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxN = int64_t(1) << 30;  // row indices inside a head are 32-bit in the kernels
 constexpr int kMaxSplits = 64;
 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -19,16 +20,15 @@ size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_common(int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale, int dtype) {
-  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
+  if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_FP16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
-  if (N % 64 != 0) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_UNSUPPORTED;
   // Grid sizes: B*H*ceil(N/64) workgroups at most; B*H must fit an int.
   if (B > kMaxWorkgroups / H) return FA_ERR_SHAPE;
   const int64_t bh = B * H;
-  if (bh > kMaxWorkgroups / (N / 64)) return FA_ERR_SHAPE;
+  if (bh > kMaxWorkgroups / ((N + 63) / 64)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -42,7 +42,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N is not positive, or the problem is too large";
     case FA_ERR_UNSUPPORTED:
-      return "FA_ERR_UNSUPPORTED: need D in {64,128}, dtype fp16/bf16, causal 0/1, N % 64 == 0, finite scale > 0";
+      return "FA_ERR_UNSUPPORTED: need D in {64,128}, dtype fp16/bf16, causal 0/1, finite scale > 0";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
@@ -88,7 +88,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   int st = check_common(B, H, N, D, causal, scale, dtype);
   if (st != FA_OK) return st;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
-  if (B * H * (N / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
+  if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;

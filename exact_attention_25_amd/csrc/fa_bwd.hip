@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t* __restr
 
 // ---------------------------------------------------------------------------
 // Tiles of 64 rows x D columns of a row-major [.., D] tensor are copied from
-// HBM straight into LDS (global_load_lds_dwordx4, 256 threads, D/32 copies
+// HBM straight into LDS (buffer_load_dwordx4 ... lds, 256 threads, D/32 copies
 // each) as 16-byte chunks in row-major order.  A tile that is read both by
 // rows and transposed uses the dual_chunk swizzle; a tile read only by rows
 // uses swz.  Copy i of wave w fills LDS chunks i*256 + 64w + lane; because
@@ -101,12 +101,17 @@ __device__ __forceinline__ int tile_src_offset(int p) {
   }
 }
 
+// `valid` = rows of the tile inside the tensor (the last tile may be partial).
 template <int D>
-__device__ __forceinline__ void copy_tile(const uint16_t* __restrict__ src, int src0, u32x4* dst, int wave) {
+__device__ __forceinline__ void copy_tile(const uint16_t* __restrict__ src, int src0, u32x4* dst, int wave,
+                                          int valid) {
   constexpr int LPT = kTileRows * (D / 8) / kThreads;
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) copy16_to_lds(src + src0 + i * kThreads * 8, dst + i * kThreads + wave * 64);
+  copy_tile_rows<D, LPT, kThreads>(src, src0, dst + wave * 64, valid);
 }
+
+// LSE * log2(e) of a query row as the backward uses it: a row that saw no
+// key (LSE = -inf) must get P = 0, which an exponent offset of +inf gives.
+__device__ __forceinline__ float lse_offset(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
 // Transposed operand read from a dual-swizzled tile: rows r..r+3 (r = the
 // lane's row for this 16-lane group), column col (see lds_read_tr16).
@@ -151,11 +156,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   const bool active = k0w < N;
   const int my_k = k0w + l32;
 
-  // Resident B operands: lane (key, g) holds K[my_k][16c+8g..+8] and V likewise.
+  // Resident B operands: lane (key, g) holds K[my_k][16c+8g..+8] and V
+  // likewise; lanes past the last key re-read row N-1 and store nothing.
   u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    const int64_t off = head + (int64_t)my_k * D + c * 16 + g * 8;
+    const int64_t off = head + (int64_t)min(my_k, (int)N - 1) * D + c * 16 + g * 8;
     kf[c] = active ? *(const u32x4*)(a.k + off) : u32x4{0, 0, 0, 0};
     vf[c] = active ? *(const u32x4*)(a.v + off) : u32x4{0, 0, 0, 0};
   }
@@ -183,17 +189,19 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   constexpr int ROW16 = 16 * RC * 16;  // bytes of 16 rows
 
   const int src0 = tile_src_offset<D, true>(wave * 64 + lane);
-  const int n_qt = (int)(N / BQ);
+  const int n_qt = (int)((N + BQ - 1) / BQ);
   const int qt_begin = CAUSAL ? (kt * BK) / BQ : 0;
   const float c2 = a.scale_log2;
 
   // LSE (times log2 e) and Delta of the next tile travel through registers of
-  // threads 0..63 and are written to LDS at the end of a step.
+  // threads 0..63 and are written to LDS at the end of a step.  Rows past the
+  // last query get an offset of +inf, hence P = 0 and dS = 0.
   float lse_n = 0.f, dl_n = 0.f;
   auto fetch_rows = [&](int qt) {
     if (tid < BQ) {
-      lse_n = a.lse[rowbase + (int64_t)qt * BQ + tid] * kLog2e;
-      dl_n = a.delta[rowbase + (int64_t)qt * BQ + tid];
+      const int row = qt * BQ + tid;
+      lse_n = row < N ? lse_offset(a.lse[rowbase + row]) : INFINITY;
+      dl_n = row < N ? a.delta[rowbase + row] : 0.f;
     }
   };
   auto put_rows = [&](float* ll, float* ld) {
@@ -265,16 +273,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     __syncthreads();  // everyone's have (and the LSE/Delta rows); tile qt-1 is done
     if (qt + 1 < n_qt) {
       fetch_rows(qt + 1);  // first, so that storing them later need not wait for the tile copies
-      copy_tile<D>(Qh + (int64_t)(qt + 1) * BQ * D, src0, Qn, wave);
-      copy_tile<D>(Gh + (int64_t)(qt + 1) * BQ * D, src0, Gn, wave);
+      const int valid = min(BQ, (int)N - (qt + 1) * BQ);
+      copy_tile<D>(Qh + (int64_t)(qt + 1) * BQ * D, src0, Qn, wave, valid);
+      copy_tile<D>(Gh + (int64_t)(qt + 1) * BQ * D, src0, Gn, wave, valid);
     }
     if (active) compute(qt, Ql, Gl, ll, ld);
     if (qt + 1 < n_qt) put_rows(lln, ldn);
   };
 
   if (qt_begin < n_qt) {
-    copy_tile<D>(Qh + (int64_t)qt_begin * BQ * D, src0, lq0, wave);
-    copy_tile<D>(Gh + (int64_t)qt_begin * BQ * D, src0, lg0, wave);
+    const int valid = min(BQ, (int)N - qt_begin * BQ);
+    copy_tile<D>(Qh + (int64_t)qt_begin * BQ * D, src0, lq0, wave, valid);
+    copy_tile<D>(Gh + (int64_t)qt_begin * BQ * D, src0, lg0, wave, valid);
     fetch_rows(qt_begin);
     put_rows(ll0, ld0);
   }
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     if (qt + 1 < n_qt) step(qt + 1, lq1, lg1, ll1, ld1, lq0, lg0, ll0, ld0);
   }
 
-  if (!active) return;
+  if (!active || my_k >= N) return;
   uint16_t* dk_row = a.dk + head + (int64_t)my_k * D;
   uint16_t* dv_row = a.dv + head + (int64_t)my_k * D;
   const float sc = a.scale;
@@ -331,15 +341,17 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const bool active = q0w < N;
   const int my_q = q0w + ql;
 
+  // Lanes past the last query re-read row N-1 and store nothing.
+  const bool real_q = my_q < N;
   u32x4 qf[D / 16], gf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    const int64_t off = head + (int64_t)my_q * D + c * 16 + g * 8;
+    const int64_t off = head + (int64_t)min(my_q, (int)N - 1) * D + c * 16 + g * 8;
     qf[c] = active ? *(const u32x4*)(a.q + off) : u32x4{0, 0, 0, 0};
     gf[c] = active ? *(const u32x4*)(a.dout + off) : u32x4{0, 0, 0, 0};
   }
-  const float lse2 = active ? a.lse[(int64_t)bh * N + my_q] * kLog2e : 0.f;
-  const float dl = active ? a.delta[(int64_t)bh * N + my_q] : 0.f;
+  const float lse2 = real_q ? lse_offset(a.lse[(int64_t)bh * N + my_q]) : 0.f;
+  const float dl = real_q ? a.delta[(int64_t)bh * N + my_q] : 0.f;
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
@@ -366,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 
   const int ksrc0 = tile_src_offset<D, true>(wave * 64 + lane);
   const int vsrc0 = tile_src_offset<D, false>(wave * 64 + lane);
-  const int n_kt_all = (int)(N / BN);
+  const int n_kt_all = (int)((N + BN - 1) / BN);
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
   const float c2 = a.scale_log2;
 
@@ -385,15 +397,25 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
         dp[kb] = mfma32<T>(*(const u32x4*)(Vb + kb * 2 * ROW16 + voff[c]), gf[c], dp[kb]);
       }
     }
-    const bool diag = CAUSAL && k0 + BN - 1 > q0w;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[kb][r], c2, -lse2));
-        if (diag && k0 + kb * 32 + acc_row(r, g) > my_q) p = 0.f;
-        dp[kb][r] = p * (dp[kb][r] - dl);
-      }
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c2, -lse2));
+    // Diagonal tile or the partial last tile (keys >= N do not exist): zero
+    // the masked probabilities.  The test is uniform, so other tiles skip it.
+    if ((CAUSAL && k0 + BN - 1 > q0w) || k0 + BN > N) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + acc_row(r, g);
+          if ((CAUSAL && key > my_q) || key >= N) s[kb][r] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[kb][r] = s[kb][r] * (dp[kb][r] - dl);
     // dQ^T += K^T dS^T, 16 keys per step (registers 8*(t%2).. of block t/2).
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
@@ -411,21 +433,22 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (kt + 1 < n_kt) {
-      copy_tile<D>(Kh + (int64_t)(kt + 1) * BN * D, ksrc0, Kn, wave);
-      copy_tile<D>(Vh + (int64_t)(kt + 1) * BN * D, vsrc0, Vn, wave);
+      const int valid = min(BN, (int)N - (kt + 1) * BN);
+      copy_tile<D>(Kh + (int64_t)(kt + 1) * BN * D, ksrc0, Kn, wave, valid);
+      copy_tile<D>(Vh + (int64_t)(kt + 1) * BN * D, vsrc0, Vn, wave, valid);
     }
     if (!active || (CAUSAL && kt * BN > q0w + 31)) return;
     compute(kt, Kl, Vl);
   };
 
-  copy_tile<D>(Kh, ksrc0, lk0, wave);
-  copy_tile<D>(Vh, vsrc0, lv0, wave);
+  copy_tile<D>(Kh, ksrc0, lk0, wave, min(BN, (int)N));
+  copy_tile<D>(Vh, vsrc0, lv0, wave, min(BN, (int)N));
   for (int kt = 0; kt < n_kt; kt += 2) {
     step(kt, lk0, lv0, lk1, lv1);
     if (kt + 1 < n_kt) step(kt + 1, lk1, lv1, lk0, lv0);
   }
 
-  if (!active) return;
+  if (!active || !real_q) return;
   uint16_t* row = a.dq + head + (int64_t)my_q * D;
   const float sc = a.scale;
 #pragma unroll

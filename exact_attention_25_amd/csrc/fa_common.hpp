@@ -143,13 +143,33 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---------------------------------------------------------------------------
 // Direct HBM -> LDS copies and transposing LDS reads (gfx950).
 // ---------------------------------------------------------------------------
-// global_load_lds_dwordx4: every lane fetches 16 bytes from its own global
-// address; lane l's bytes land at lds_wave_base + 16*l.  lds_wave_base must
-// be the same for the whole wave.  Completion is tracked by vmcnt.
-__device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// buffer_load_dwordx4 ... lds: every lane fetches 16 bytes at its own byte
+// offset into a buffer resource; lane l's bytes land at lds_wave_base + 16*l,
+// and lds_wave_base must be the same for the whole wave.  Completion is
+// tracked by vmcnt.  A raw buffer resource (stride 0) of `bytes` bytes makes
+// every load at or past byte `bytes` return zero without touching memory,
+// which is how partial tiles are read.  The descriptor lives in scalar
+// registers when `base` and `bytes` are wave-uniform.  Word 3 (0x00020000)
+// is the gfx9 family's data-format field for untyped 32-bit loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
+
+// Direct copy of one 64-row tile of a row-major [rows, D] tensor by NT
+// threads: copy i of this lane reads the 16-byte chunk at element offset
+// src0 + i*NT*8 of the tile and lands at dst + i*NT (dst already includes
+// the wave's 64-chunk offset).  Only `valid` rows (1 .. 64) of the tile lie
+// inside the tensor; chunks of later rows read as zero, and callers mask
+// those rows out of the result.
+template <int D, int LPT, int NT>
+__device__ __forceinline__ void copy_tile_rows(const uint16_t* tile, int src0, u32x4* dst, int valid) {
+  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(tile, valid * D * 2);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + i * NT), 16,
+                                             src0 * 2, i * NT * 16, 0, 0);
+}
+
 // Wait until this wave's outstanding global loads (including LDS-bound ones)
 // have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

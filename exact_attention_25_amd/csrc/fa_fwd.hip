@@ -16,7 +16,7 @@
 //    32 queries per MFMA).  With QB = 2 every K or V^T fragment read from
 //    LDS feeds two independent MFMAs, halving LDS traffic per FLOP.
 //  * Keys and values stream in tiles of 64 keys straight from HBM into a
-//    double-buffered LDS ring (global_load_lds_dwordx4: no VGPR staging), one
+//    double-buffered LDS ring (buffer_load_dwordx4 ... lds: no VGPR staging), one
 //    workgroup barrier per tile.  Both tiles stay row-major with an XOR
 //    swizzle of 16-byte chunks; K fragments are read with ds_read_b128 and
 //    the V^T fragments of O^T = V^T P^T with the transposing
@@ -93,16 +93,17 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   const uint16_t* __restrict__ Vh = a.v + head;
 
   const int q0w = qt * BM + wave * WQ;  // first query of this wave
-  const bool active = q0w < N;          // N % 64 == 0: whole wave in or out
+  const bool active = q0w < N;          // the wave has at least one real query
 
   // Q^T operand fragments: lane (ql, g) of block qb holds
-  // Q[q0w + 32qb + ql][16c + 8g .. +8].
+  // Q[q0w + 32qb + ql][16c + 8g .. +8].  Lanes past the last query re-read
+  // row N-1; their results are never stored.
   u32x4 qf[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-      qf[qb][c] = active ? *(const u32x4*)(Qh + (int64_t)(q0w + 32 * qb + ql) * D + c * 16 + g * 8)
+      qf[qb][c] = active ? *(const u32x4*)(Qh + (int64_t)min(q0w + 32 * qb + ql, (int)N - 1) * D + c * 16 + g * 8)
                          : u32x4{0, 0, 0, 0};
 
   f32x16 oacc[QB][D / 32];
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     l_run[qb] = 0.f;
   }
 
-  const int n_kt_all = (int)(N / BN);
+  const int n_kt_all = (int)((N + BN - 1) / BN);  // the last tile may be partial
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
   // Key tiles of this workgroup: all visible ones, or this split's share.
   const int kt_begin = SPLIT ? (int)(((int64_t)split * n_kt_all) / a.n_splits) : 0;
@@ -129,14 +130,10 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   const int vr0 = p0 / RC;
   const int vsrc0 = vr0 * D + ((p0 % RC) ^ ((vr0 & (RC == 16 ? 7 : 3)) << 1)) * 8;
   auto load_k = [&](int kt, u32x4* dst) {
-    const uint16_t* src = Kh + (int64_t)kt * BN * D + ksrc0;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) copy16_to_lds(src + i * NT * 8, dst + i * NT + wave * 64);
+    copy_tile_rows<D, LPT, NT>(Kh + (int64_t)kt * BN * D, ksrc0, dst + wave * 64, min(BN, (int)N - kt * BN));
   };
   auto load_v = [&](int kt, u32x4* dst) {
-    const uint16_t* src = Vh + (int64_t)kt * BN * D + vsrc0;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) copy16_to_lds(src + i * NT * 8, dst + i * NT + wave * 64);
+    copy_tile_rows<D, LPT, NT>(Vh + (int64_t)kt * BN * D, vsrc0, dst + wave * 64, min(BN, (int)N - kt * BN));
   };
 
   // S^T = K Q^T for one 64-key tile: two 32-key blocks, K rows read in
@@ -181,16 +178,20 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     const int k0 = kt * BN;
     if (!active || (CAUSAL && k0 > q0w + WQ - 1)) return;  // nothing visible
 
-    // Diagonal tile: mask before the max (a block wholly above its queries
-    // is masked entirely and contributes zero probabilities).
-    if (CAUSAL && k0 + BN - 1 > q0w) {
+    // Diagonal tile, or the partial last tile: mask before the max (a block
+    // wholly above its queries is masked entirely and contributes zero
+    // probabilities; keys >= N do not exist).  Both tests are uniform, so
+    // full tiles below the diagonal take no per-element branch.
+    if ((CAUSAL && k0 + BN - 1 > q0w) || k0 + BN > N) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (k0 + kb * 32 + acc_row(r, g) > q0w + 32 * qb + ql) s[qb][kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + acc_row(r, g);
+            if ((CAUSAL && key > q0w + 32 * qb + ql) || key >= N) s[qb][kb][r] = -INFINITY;
+          }
     }
 
     // The reference max r_raw is always one of the raw scores (exact).  In
@@ -322,6 +323,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       const int my_q = q0w + 32 * qb + ql;
       const float l_tot = xhalf_sum(l_run[qb]);
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (my_q >= N) continue;
       const int64_t row = (int64_t)bh * N + my_q;
       float* Orow = a.part_o + ((int64_t)split * rows + row) * D;
 #pragma unroll
@@ -342,6 +344,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     const int my_q = q0w + 32 * qb + ql;
     const float l_tot = xhalf_sum(l_run[qb]);
     const float inv = 1.f / l_tot;
+    if (my_q >= N) continue;  // lanes past the last query
     uint16_t* Orow = a.o + head + (int64_t)my_q * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

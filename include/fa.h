@@ -28,11 +28,18 @@
  *   - LSE and the backward workspace: contiguous FP32 [B, H, N], 16-byte
  *     aligned.
  *   - Outputs must not alias inputs or each other.
- *   - Supported: D in {64, 128}; N a positive multiple of 64; B, H >= 1;
- *     B*H*N*D < 2^31 * 64; scale finite and > 0.  Anything else is rejected
- *     with an error code before any work is enqueued -- never silently
- *     computed ("CUDA FlashAttention ...", §9: unsupported shapes fall back
- *     explicitly).
+ *   - Supported: D in {64, 128}; any 1 <= N <= 2^30; B, H >= 1;
+ *     B*H*ceil(N/64) < 2^31; scale finite and > 0.  Anything else is
+ *     rejected with an error code before any work is enqueued -- never
+ *     silently computed ("CUDA FlashAttention ...", §9: unsupported shapes
+ *     fall back explicitly).
+ *   - N need not be a multiple of the 64-row tile.  The last, partial tile
+ *     is read with every row index clamped to N-1, so no load leaves the
+ *     tensors, and its missing keys are masked to -inf before the row max;
+ *     rows past N are never written ("FlashAttention dataflow and
+ *     engineering validation on MI50", §6.1: the boundary tile must be
+ *     cropped and masked rather than read past the end; "CUDA
+ *     FlashAttention ...", §5.4: ragged tails take masked loads).
  *   - Numerics: products on fp16/bf16 MFMA with FP32 accumulation; running
  *     max, sum and output accumulators in FP32 ("CUDA FlashAttention ...", §2);
  *     outputs rounded to the storage type with round-to-nearest-even.
@@ -55,8 +62,8 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
-  FA_ERR_SHAPE = 2,       /* B, H or N <= 0, or the index space is too large     */
-  FA_ERR_UNSUPPORTED = 3, /* D, dtype, causal flag, N % 64 or scale unsupported  */
+  FA_ERR_SHAPE = 2,       /* B, H or N <= 0, N > 2^30, or the grid is too large   */
+  FA_ERR_UNSUPPORTED = 3, /* D, dtype, causal flag or scale unsupported          */
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
   FA_ERR_WORKSPACE = 5,   /* backward workspace missing or smaller than needed   */
   FA_ERR_HIP = 6          /* the HIP runtime rejected a launch                   */

@@ -65,7 +65,7 @@ def test_fwd_null(name):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2),
     (dict(D=96), 3), (dict(D=256), 3), (dict(dtype=2), 3), (dict(causal=2), 3),
-    (dict(N=1025), 3), (dict(N=100), 3), (dict(scale=0.0), 3), (dict(scale=-1.0), 3),
+    (dict(N=(1 << 30) + 1), 2), (dict(scale=0.0), 3), (dict(scale=-1.0), 3),
     (dict(scale=float("inf")), 3), (dict(scale=float("nan")), 3),
     (dict(q=P + 2), 4), (dict(o=P + 8), 4), (dict(lse=P + 4), 4),
     (dict(B=1 << 40, H=1 << 30), 2),
@@ -80,7 +80,7 @@ def test_bwd_null(name):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(N=64 * 3 + 1), 3), (dict(D=32), 3), (dict(dk=P + 2), 4), (dict(ws=None), 5),
+    (dict(N=(1 << 30) + 64), 2), (dict(D=32), 3), (dict(dk=P + 2), 4), (dict(ws=None), 5),
     (dict(wsb=4 * 2 * 128 - 1), 5), (dict(ws=P + 4), 4), (dict(H=0), 2),
 ])
 def test_bwd_rejects(kw, code):
@@ -90,7 +90,8 @@ def test_bwd_rejects(kw, code):
 def test_workspace_bytes():
     assert fb.bwd_workspace_bytes(2, 3, 128, 64, 1, 0) == 2 * 3 * 128 * 4
     assert fb.bwd_workspace_bytes(1, 1, 64, 128, 0, 1) == 256
-    assert fb.bwd_workspace_bytes(1, 1, 100, 64, 0, 0) == 0
+    assert fb.bwd_workspace_bytes(1, 1, 100, 64, 0, 0) == 512  # any N: 400 bytes, rounded up
+    assert fb.bwd_workspace_bytes(1, 1, 100, 96, 0, 0) == 0
 
 
 def split(**kw):
@@ -102,7 +103,7 @@ def split(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(q=None), 1), (dict(lse=None), 1), (dict(s=0), 3), (dict(s=65), 3), (dict(N=200), 3),
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(s=0), 3), (dict(s=65), 3), (dict(N=-200), 2),
     (dict(ws=None), 5), (dict(wsb=1000), 5), (dict(ws=P + 8), 4), (dict(v=P + 2), 4), (dict(B=0), 2),
 ])
 def test_splitkv_rejects(kw, code):

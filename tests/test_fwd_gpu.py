@@ -134,5 +134,6 @@ def test_fwd_rejects_misaligned_and_unsupported_on_device():
     st = binding.fa_fwd(bad.data_ptr(), good.data_ptr(), good.data_ptr(), o.data_ptr(), lse.data_ptr(),
                         1, 1, 128, 64, 0, 0.125, 0, torch.cuda.current_stream().cuda_stream)
     assert st == 4
+    d96 = torch.zeros(1, 1, 129, 96, dtype=torch.float16, device="cuda")
     with pytest.raises(binding.FaError):
-        fa.fwd(good, good, good)  # N = 129 is not a multiple of 64
+        fa.fwd(d96, d96, d96)  # head dimension 96 is not supported
