@@ -18,12 +18,15 @@ written from the definitions on these pages (cited by title and section):
   (jefxiong.cn) -- §3.1 safe softmax, §3.2 online recurrence and LSE, §3.3
   backward with the scale factor, §4.5 causal block skipping.
 * [FA-MI50]  "FlashAttention dataflow and engineering validation on MI50"
-  (mpbf.cn/news/61284) -- §2.2 worked example, §3.3 backward correction term.
+  (mpbf.cn/news/61284) -- §2.2 worked example, §3.3 backward correction term,
+  §4.3 block-level flags of padding masks, §5.1 random mask patterns.
 
 Modules
 -------
-``attention``  plain-definition forward / backward (materialised rows),
-               online tiled forward, state merge, pure-Python brute force.
+``attention``  plain-definition forward / backward (materialised rows,
+               optional key-padding mask), online tiled forward, state
+               merge, key-split partial states, block-level mask flags,
+               pure-Python brute force.
 
 Every function in ``attention`` is pinned by ``tests/test_oracle.py``; none is
 "parity unpinned".
@@ -39,4 +42,5 @@ from .attention import (  # noqa: F401
     merge_lse,
     brute_force_forward,
     causal_tile_count,
+    key_tile_words,
 )

@@ -13,6 +13,14 @@ Conventions (shared with the C ABI only by *meaning*, not by code):
   aligned mask with -inf ([FA-CUDA] §1).
 * The log-sum-exp uses the natural logarithm: LSE_i = m_i + ln l_i
   ([FA-WHY] §3.2, last remark of the section).
+* ``key_mask`` (optional, ``[B, N]``, nonzero = visible) is a key-padding
+  mask: score S_ij of batch element b is -inf where key j is not visible,
+  before the max, like the causal mask.  It is how padded variable-length
+  batches are described ([FA-MI50] §4.3: padding masks of variable-length
+  sequences; §5.1: random mask patterns as a test).  A row that sees no
+  visible key has no defined softmax; the reading taken here is O_i = 0 and
+  LSE_i = -inf, and such a row contributes nothing to any gradient (the -inf
+  guard of [FA-CUDA] §6: with m = -inf nothing is exponentiated against it).
 
 Source titles: [FA-CUDA] "CUDA FlashAttention: from online softmax to the
 long-sequence IO limit"; [FA-ALGO] "FlashAttention algorithm details" (ch. 4);
@@ -42,12 +50,13 @@ def _check4(*arrays):
 # ---------------------------------------------------------------------------
 # Plain definition: two-pass safe softmax over complete, materialised rows.
 # ---------------------------------------------------------------------------
-def _scores_block(qh, kh, i0, i1, causal, scale, rows=None):
+def _scores_block(qh, kh, i0, i1, causal, scale, rows=None, vis=None):
     """Score rows S = scale * Q K^T with the causal -inf mask applied.
 
     Rows are query indices i0..i1-1, or the explicit index array ``rows``.
     With ``causal`` the block only ever sees keys 0..max(row), so it is
     truncated there; the truncated columns would all be -inf anyway.
+    ``vis`` (bool [N]) sets the columns of invisible keys to -inf.
     Definition: [FA-CUDA] §1 (S = QK^T/sqrt(D) + M, M_ij = -inf for j > i).
     """
     if rows is None:
@@ -57,19 +66,33 @@ def _scores_block(qh, kh, i0, i1, causal, scale, rows=None):
     if causal:
         cols = np.arange(nk)[None, :]
         s = np.where(cols > rows[:, None], NEG_INF, s)
+    if vis is not None:
+        s = np.where(vis[None, :nk], s, NEG_INF)
     return s, nk
 
 
 def _safe_softmax_rows(s):
     """Safe softmax of complete rows: subtract the row max, exponentiate,
-    normalise ([FA-WHY] §3.1).  Returns (P, m, l) with l = sum exp(s - m)."""
+    normalise ([FA-WHY] §3.1).  Returns (P, m, l) with l = sum exp(s - m).
+    A row whose scores are all -inf gets P = 0, m = -inf and l = 0."""
     m = s.max(axis=1)
-    e = np.exp(s - m[:, None])
+    seen = np.isfinite(m)
+    e = np.exp(s - np.where(seen, m, 0.0)[:, None])
     l = e.sum(axis=1)
-    return e / l[:, None], m, l
+    return e / np.where(seen, l, 1.0)[:, None], m, l
 
 
-def attention_forward(q, k, v, causal, scale, row_block=256, rows=None):
+def _visibility(key_mask, B, N):
+    """key_mask [B, N] -> bool array, or None for no mask."""
+    if key_mask is None:
+        return None
+    vis = np.asarray(key_mask) != 0
+    if vis.shape != (B, N):
+        raise ValueError("key_mask must be [B, N] = %r, got %r" % ((B, N), vis.shape))
+    return vis
+
+
+def attention_forward(q, k, v, causal, scale, row_block=256, rows=None, key_mask=None):
     """O = softmax(scale * Q K^T + M) V and LSE, by the plain definition.
 
     For every (b, h) and every block of ``row_block`` query rows the complete
@@ -80,12 +103,15 @@ def attention_forward(q, k, v, causal, scale, row_block=256, rows=None):
 
     ``rows``: optional 1-D array of query indices; then only those rows are
     computed (for every head) and the outputs have len(rows) in place of N.
+    ``key_mask``: optional [B, N] key-padding mask (see the module notes);
+    rows without a visible key get O = 0 and LSE = -inf.
 
     Returns (O, LSE) as float64 arrays of shape [B,H,R,D] and [B,H,R].
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     _check4(q, k, v)
     B, H, N, D = q.shape
+    vis = _visibility(key_mask, B, N)
     sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = sel.shape[0]
     o = np.empty((B, H, R, D))
@@ -95,10 +121,11 @@ def attention_forward(q, k, v, causal, scale, row_block=256, rows=None):
             qh, kh, vh = q[b, h], k[b, h], v[b, h]
             for r0 in range(0, R, row_block):
                 r1 = min(R, r0 + row_block)
-                s, nk = _scores_block(qh, kh, 0, 0, causal, scale, rows=sel[r0:r1])
+                s, nk = _scores_block(qh, kh, 0, 0, causal, scale, rows=sel[r0:r1],
+                                      vis=None if vis is None else vis[b])
                 p, m, l = _safe_softmax_rows(s)
                 o[b, h, r0:r1] = p @ vh[:nk]
-                lse[b, h, r0:r1] = m + np.log(l)
+                lse[b, h, r0:r1] = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
     return o, lse
 
 
@@ -116,7 +143,7 @@ def attention_probs(q, k, causal, scale):
     return p
 
 
-def attention_backward(q, k, v, do, causal, scale, row_block=256):
+def attention_backward(q, k, v, do, causal, scale, row_block=256, key_mask=None):
     """dQ, dK, dV of L with dL/dO = ``do``, by the plain definition.
 
     With P the forward probabilities and G = dO:
@@ -125,11 +152,13 @@ def attention_backward(q, k, v, do, causal, scale, row_block=256):
     [FA-WHY] §3.3 states these formulas including the scale factor;
     [FA-ALGO] §4.3.1 gives the same ones with the scale omitted.  P is
     materialised in float64 a block of query rows at a time; sums over
-    query rows are split over those blocks.
+    query rows are split over those blocks.  With ``key_mask``, P is the
+    masked softmax (zero for invisible keys and for rows with no visible key).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     _check4(q, k, v, do)
     B, H, N, D = q.shape
+    vis = _visibility(key_mask, B, N)
     dq = np.zeros((B, H, N, D))
     dk = np.zeros((B, H, N, D))
     dv = np.zeros((B, H, N, D))
@@ -138,7 +167,7 @@ def attention_backward(q, k, v, do, causal, scale, row_block=256):
             qh, kh, vh, gh = q[b, h], k[b, h], v[b, h], do[b, h]
             for i0 in range(0, N, row_block):
                 i1 = min(N, i0 + row_block)
-                s, nk = _scores_block(qh, kh, i0, i1, causal, scale)
+                s, nk = _scores_block(qh, kh, i0, i1, causal, scale, vis=None if vis is None else vis[b])
                 p, _, _ = _safe_softmax_rows(s)
                 g = gh[i0:i1]
                 dv[b, h, :nk] += p.T @ g
@@ -303,21 +332,59 @@ def causal_tile_count(n, block):
     return count
 
 
+def key_tile_words(key_mask, block=64):
+    """Block-level flags of a key-padding mask: [FA-MI50] §4.3 asks that a
+    padding mask be compressed beforehand into per-block marks, so that the
+    block loop branches once per block instead of per element.
+
+    For batch element b and key tile t (keys block*t .. block*t + block-1),
+    bit j of words[b][t] is set iff key block*t + j exists (< N) and is
+    visible.  A zero word is a tile to skip, an all-ones word one that needs
+    no element test.  Returns (words: list of lists of Python ints,
+    tiles: for each b, the ascending indices of tiles with a nonzero word).
+    Plain loops over the mask, one key at a time.
+    """
+    m = np.asarray(key_mask)
+    B, N = m.shape
+    T = -(-N // block)
+    words, tiles = [], []
+    for b in range(B):
+        row_words, row_tiles = [], []
+        for t in range(T):
+            w = 0
+            for j in range(block):
+                key = block * t + j
+                if key < N and m[b, key] != 0:
+                    w |= 1 << j
+            row_words.append(w)
+            if w != 0:
+                row_tiles.append(t)
+        words.append(row_words)
+        tiles.append(row_tiles)
+    return words, tiles
+
+
 # ---------------------------------------------------------------------------
 # Pure-Python brute force for tiny inputs.
 # ---------------------------------------------------------------------------
-def brute_force_forward(q, k, v, causal, scale):
+def brute_force_forward(q, k, v, causal, scale, visible=None):
     """Attention of one head with Python floats, math.exp and math.fsum.
 
     q, k, v: nested sequences [N][D] (N <= 8 expected).  Direct transcription
     of the definition ([FA-CUDA] §1, safe softmax per [FA-WHY] §3.1), no
-    numpy.  Returns (O as list of lists, LSE as list).
+    numpy.  ``visible``: optional sequence of N truth values; only those keys
+    take part.  A row with no key gets O = 0 and LSE = -inf.
+    Returns (O as list of lists, LSE as list).
     """
     n = len(q)
     d = len(q[0])
     out, lse = [], []
     for i in range(n):
-        keys = range(i + 1) if causal else range(n)
+        keys = [j for j in (range(i + 1) if causal else range(n)) if visible is None or visible[j]]
+        if not keys:
+            out.append([0.0] * d)
+            lse.append(-math.inf)
+            continue
         s = [scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in keys]
         m = max(s)
         e = [math.exp(x - m) for x in s]

@@ -20,6 +20,7 @@ from oracle import (
     attention_probs,
     brute_force_forward,
     causal_tile_count,
+    key_tile_words,
     merge_states,
     online_forward,
 )
@@ -334,3 +335,116 @@ def test_partial_of_unseen_keys_is_empty():
     o1, lse1 = attention_partial(q, k, v, False, 0.5, 3, 4)
     assert np.abs(o1[0, 0] - v[0, 0, 3]).max() < 1e-15
     assert np.abs(lse1[0, 0] - 0.5 * (q[0, 0] @ k[0, 0, 3])).max() < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Key-padding masks (variable-length batches) and their block-level flags
+# --------------------------------------------------------------------------
+def _mask(seed, b, n, p=0.6):
+    return (np.random.default_rng(seed).random((b, n)) < p).astype(np.uint8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_visible_mask_changes_nothing(causal):
+    q, k, v = _rand(400, 2, 2, 70, 8), _rand(401, 2, 2, 70, 8), _rand(402, 2, 2, 70, 8)
+    a = attention_forward(q, k, v, causal, 0.3)
+    b = attention_forward(q, k, v, causal, 0.3, key_mask=np.ones((2, 70), np.uint8))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_masked_keys_equal_deleted_keys():
+    # without a causal mask, an invisible key is the same as no key at all
+    n, d = 50, 8
+    q, k, v = _rand(410, 1, 1, n, d), _rand(411, 1, 1, n, d), _rand(412, 1, 1, n, d)
+    mask = _mask(413, 1, n)
+    keep = mask[0] != 0
+    o, lse = attention_forward(q, k, v, False, 0.4, key_mask=mask)
+    o2, lse2 = attention_forward(q, k[:, :, keep], v[:, :, keep], False, 0.4)
+    assert np.abs(o - o2).max() < 1e-14 and np.abs(lse - lse2).max() < 1e-13
+
+
+@pytest.mark.parametrize("n", [1, 3, 8])
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_brute_force_agrees(n, causal):
+    d = 4
+    q, k, v = _rand(420 + n, n, d), _rand(430 + n, n, d), _rand(440 + n, n, d)
+    for seed in range(4):
+        vis = _mask(450 + seed, 1, n, 0.5)
+        ob, lb = brute_force_forward(q.tolist(), k.tolist(), v.tolist(), causal, 0.5, visible=vis[0].tolist())
+        o, lse = attention_forward(_heads(q), _heads(k), _heads(v), causal, 0.5, key_mask=vis)
+        assert np.abs(o[0, 0] - np.array(ob)).max() < 1e-14
+        lb = np.array(lb)
+        assert np.array_equal(np.isneginf(lse[0, 0]), np.isneginf(lb))
+        fin = np.isfinite(lb)
+        assert np.abs(lse[0, 0][fin] - lb[fin]).max(initial=0.0) < 1e-14
+
+
+def test_row_without_visible_key_is_zero_with_minus_inf_lse():
+    n, d = 6, 4
+    q, k, v = _rand(460, 1, 1, n, d), _rand(461, 1, 1, n, d), _rand(462, 1, 1, n, d)
+    mask = np.array([[0, 0, 1, 1, 0, 1]], np.uint8)
+    o, lse = attention_forward(q, k, v, True, 1.0, key_mask=mask)
+    # causal rows 0 and 1 see only keys 0..1, both invisible
+    assert np.array_equal(o[0, 0, :2], np.zeros((2, d))) and np.all(np.isneginf(lse[0, 0, :2]))
+    # row 2 sees only key 2: O = v_2, LSE = s_22
+    assert np.abs(o[0, 0, 2] - v[0, 0, 2]).max() < 1e-15
+    assert abs(lse[0, 0, 2] - float(q[0, 0, 2] @ k[0, 0, 2])) < 1e-14
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse[0, 0, 2:]))
+
+
+def test_length_mask_equals_shorter_sequences():
+    # a right-padded variable-length batch: element b holds L_b real tokens
+    n, d, lens = 40, 8, [40, 17, 1]
+    q, k, v = _rand(470, 3, 2, n, d), _rand(471, 3, 2, n, d), _rand(472, 3, 2, n, d)
+    mask = (np.arange(n)[None, :] < np.array(lens)[:, None]).astype(np.uint8)
+    for causal in (False, True):
+        o, lse = attention_forward(q, k, v, causal, 0.3, key_mask=mask)
+        for b, L in enumerate(lens):
+            sl = slice(0, L)
+            o2, lse2 = attention_forward(q[b:b + 1, :, sl], k[b:b + 1, :, sl], v[b:b + 1, :, sl], causal, 0.3)
+            assert np.abs(o[b:b + 1, :, sl] - o2).max() < 1e-14
+            assert np.abs(lse[b:b + 1, :, sl] - lse2).max() < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_backward_matches_finite_differences(causal):
+    n, d = 7, 3
+    q, k, v = _rand(480, 1, 1, n, d), _rand(481, 1, 1, n, d), _rand(482, 1, 1, n, d)
+    do = _rand(483, 1, 1, n, d)
+    mask = np.array([[0, 1, 1, 0, 1, 0, 1]], np.uint8)  # causal row 0 has no key
+    scale = 0.7
+    grads = attention_backward(q, k, v, do, causal, scale, key_mask=mask)
+
+    def loss(q_, k_, v_):
+        o, _ = attention_forward(q_, k_, v_, causal, scale, key_mask=mask)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for gi, name in enumerate("qkv"):
+        base = [q, k, v]
+        num = np.zeros_like(base[gi])
+        for idx in np.ndindex(base[gi].shape):
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[gi][idx] += h
+            minus[gi][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        assert np.abs(num - grads[gi]).max() < 1e-8, name
+    # invisible keys receive exactly zero gradient; so does a row with no key
+    hidden = mask[0] == 0
+    assert np.all(grads[1][0, 0, hidden] == 0) and np.all(grads[2][0, 0, hidden] == 0)
+    if causal:
+        assert np.all(grads[0][0, 0, 0] == 0)
+
+
+def test_key_tile_words_by_hand():
+    n = 130  # tiles of 64, 64 and 2 keys
+    words, tiles = key_tile_words(np.ones((1, n), np.uint8))
+    assert words == [[(1 << 64) - 1, (1 << 64) - 1, 0b11]] and tiles == [[0, 1, 2]]
+    words, tiles = key_tile_words(np.zeros((1, n), np.uint8))
+    assert words == [[0, 0, 0]] and tiles == [[]]
+    m = np.zeros((2, n), np.uint8)
+    m[0, 65] = 1
+    m[1, 0] = m[1, 63] = m[1, 129] = 1
+    words, tiles = key_tile_words(m)
+    assert words == [[0, 2, 0], [1 | (1 << 63), 0, 0b10]] and tiles == [[1], [0, 2]]
