@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--mode bench|copy|fwd-only|bwd-only]
+                    [--splits S] [--mask lengths|random|blocks|all]
 
 Default workload: causal fp16 attention forward, B=1 H=32 N=8192 D=128 (the
 headline metric: causal forward TFLOP/s and its fraction of the dense fp16
@@ -18,6 +19,10 @@ the float64 CPU oracle on a bounded sample of the same workload.
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters can be calibrated against a
 kernel whose HBM traffic is known.
 --mode fwd-only / bwd-only launch just that pass K times (for profiling).
+--splits S times fa_fwd_splitkv with S key splits instead of fa_fwd.
+--mask KIND times fa_fwd_masked / fa_bwd_masked with a seeded key-padding
+mask (lengths / random / blocks / all); TFLOP/s then count only the visible
+(query, key) pairs, and the one-off tile-table build is reported apart.
 """
 
 import argparse
@@ -55,6 +60,9 @@ def parse():
     p.add_argument("--mode", default="bench", choices=["bench", "copy", "fwd-only", "bwd-only"])
     p.add_argument("--splits", type=int, default=0,
                    help="time fa_fwd_splitkv with this many key splits (split pass + merge) instead of fa_fwd")
+    p.add_argument("--mask", default=None, choices=["lengths", "random", "blocks", "all"],
+                   help="time fa_fwd_masked / fa_bwd_masked with a seeded key-padding mask of this kind; "
+                        "FLOPs then count only visible (query, key) pairs")
     return p.parse_args()
 
 
@@ -153,7 +161,33 @@ def main():
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    if args.splits > 0:
+    tiles = None
+    flop_fraction = 1.0  # visible (query, key) pairs / pairs of the unmasked workload
+    mask_ms = None
+    if args.mask:
+        from exact_attention_25_amd.inputs import make_key_mask
+        m = make_key_mask(w.B, w.N, args.mask, seed=w.seed, p=0.5)
+        vis = m.astype(np.int64)
+        if w.causal:
+            pairs = int(np.cumsum(vis, axis=1).sum())  # row i sees visible keys j <= i
+            full = w.B * w.N * (w.N + 1) // 2
+        else:
+            pairs = int(vis.sum()) * w.N
+            full = w.B * w.N * w.N
+        flop_fraction = pairs / full
+        mask_dev = torch.from_numpy(m).to(dev)
+        tiles = fa.mask_tiles(mask_dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            fa.mask_tiles(mask_dev)
+        torch.cuda.synchronize()
+        mask_ms = (time.perf_counter() - t0) / 10 * 1e3
+
+    if args.mask:
+        def run_fwd():
+            fa.fwd_masked(q, k, v, tiles, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    elif args.splits > 0:
         split_ws = torch.empty(max(256, fa.fwd_splitkv_workspace_bytes(
             w.B, w.H, w.N, w.D, w.causal, 0 if w.dtype == "fp16" else 1, args.splits)), dtype=torch.uint8, device=dev)
 
@@ -167,6 +201,8 @@ def main():
                      dtype=torch.uint8, device=dev)
 
     def run_bwd():
+        if args.mask:
+            return fa.bwd_masked(q, k, v, o, lse, do, tiles, causal=w.causal, scale=w.scale, workspace=ws)
         return fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
 
     if args.mode in ("fwd-only", "bwd-only"):
@@ -192,11 +228,17 @@ def main():
         return e0.elapsed_time(e1) / steps  # ms per call
 
     ms = timed(run_fwd, args.steps, args.warmup)
-    tflops = w.fwd_flops() / (ms * 1e-3) / 1e12
+    tflops = flop_fraction * w.fwd_flops() / (ms * 1e-3) / 1e12
     bwd_ms = timed(run_bwd, max(1, args.steps // 2), max(1, args.warmup // 2))
-    bwd_tflops = w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
+    bwd_tflops = flop_fraction * w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
 
-    traffic = load_traffic(w.name) if args.splits == 0 else None
+    traffic = load_traffic(w.name) if args.splits == 0 and not args.mask else None
+    if args.mask:
+        kernel = "fwd_kernel<%d,%s,key mask>" % (w.D, "causal" if w.causal else "full")
+    elif args.splits > 0:
+        kernel = "fwd_kernel<%d,%s> split x%d + merge_kernel" % (w.D, "causal" if w.causal else "full", args.splits)
+    else:
+        kernel = "fwd_kernel<%d,%s>" % (w.D, "causal" if w.causal else "full")
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -217,8 +259,7 @@ def main():
         "pct_mfma_peak": round(100 * tflops / PEAK_TFLOPS_FP16, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": ("fwd_kernel<%d,%s> split x%d + merge_kernel" % (w.D, "causal" if w.causal else "full", args.splits)
-                       if args.splits > 0 else "fwd_kernel<%d,%s>" % (w.D, "causal" if w.causal else "full")),
+            "kernel": kernel,
             "achieved": round(tflops, 2),
             "peak": PEAK_TFLOPS_FP16,
             "unit": "TFLOP/s",
@@ -233,6 +274,11 @@ def main():
             "flops_counted": "10*B*H*N^2*D (causal: half): five N x N x D products",
         },
     }
+    if args.mask:
+        rec["mask"] = {"kind": args.mask, "visible_pair_fraction": round(flop_fraction, 4),
+                       "mask_tiles_ms": round(mask_ms, 4),
+                       "flops_counted": "visible (query, key) pairs only"}
+        rec["vs_baseline"] = None
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -58,6 +58,16 @@ def load_library():
     lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_mask_tiles_bytes.argtypes = [_i64, _i64]
+    lib.fa_mask_tiles_bytes.restype = ctypes.c_size_t
+    lib.fa_mask_tiles.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_size_t, _vp]
+    lib.fa_mask_tiles.restype = ctypes.c_int
+    lib.fa_fwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, _vp]
+    lib.fa_fwd_masked.restype = ctypes.c_int
+    lib.fa_bwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.fa_bwd_masked.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -91,6 +101,25 @@ def fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits):
 
 def bwd_workspace_bytes(B, H, N, D, causal, dtype):
     return int(load_library().fa_bwd_workspace_bytes(B, H, N, D, int(causal), int(dtype)))
+
+
+def fa_mask_tiles_bytes(B, N):
+    return int(load_library().fa_mask_tiles_bytes(B, N))
+
+
+def fa_mask_tiles(key_mask, B, N, tiles, tiles_bytes, stream):
+    return load_library().fa_mask_tiles(key_mask, B, N, tiles, tiles_bytes, stream)
+
+
+def fa_fwd_masked(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, tiles, stream):
+    return load_library().fa_fwd_masked(q, k, v, o, lse, B, H, N, D, int(causal), float(scale), int(dtype),
+                                        tiles, stream)
+
+
+def fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, tiles,
+                  workspace, workspace_bytes, stream):
+    return load_library().fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, int(causal),
+                                        float(scale), int(dtype), tiles, workspace, workspace_bytes, stream)
 
 
 # ---- torch-tensor convenience wrappers ----
@@ -191,4 +220,69 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def mask_tiles(key_mask):
+    """Tile table (uint8 device tensor) of a [B, N] key-padding mask (bool or
+    uint8 device tensor, nonzero = visible), built by fa_mask_tiles."""
+    import torch
+    if key_mask.dim() != 2 or not key_mask.is_cuda:
+        raise ValueError("key_mask must be a [B, N] device tensor")
+    m = key_mask.to(torch.uint8).contiguous()
+    B, N = m.shape
+    need = fa_mask_tiles_bytes(B, N)
+    if need == 0:
+        raise ValueError("unsupported mask shape %s" % (tuple(m.shape),))
+    tiles = torch.empty(need, dtype=torch.uint8, device=m.device)
+    st = fa_mask_tiles(m.data_ptr(), B, N, tiles.data_ptr(), need, _stream_handle(m.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_mask_tiles")
+    return tiles
+
+
+def fwd_masked(q, k, v, tiles, causal=False, scale=None, out=None, lse=None):
+    """fa_fwd_masked with the tile table from mask_tiles().  Returns (o, lse);
+    rows with no visible key get o = 0 and lse = -inf."""
+    import torch
+    B, H, N, D = q.shape
+    _check({"q": q, "k": k, "v": v}, q.shape, q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check({"out": out}, q.shape, q.dtype, q.device)
+    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
+    if tiles.numel() < fa_mask_tiles_bytes(B, N):
+        raise ValueError("tile table too small for B=%d N=%d" % (B, N))
+    st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, H, N, D, causal, scale, _dtype_code(q), tiles.data_ptr(), _stream_handle(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_masked")
+    return out, lse
+
+
+def bwd_masked(q, k, v, o, lse, dout, tiles, causal=False, scale=None, workspace=None):
+    """fa_bwd_masked: gradients of fwd_masked with the same tile table."""
+    import torch
+    B, H, N, D = q.shape
+    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
+    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if tiles.numel() < fa_mask_tiles_bytes(B, N):
+        raise ValueError("tile table too small for B=%d N=%d" % (B, N))
+    code = _dtype_code(q)
+    need = bwd_workspace_bytes(B, H, N, D, causal, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    st = fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, causal, scale, code,
+                       tiles.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       _stream_handle(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_masked")
     return dq, dk, dv

@@ -32,6 +32,86 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t D, int causal, float s
   return FA_OK;
 }
 
+// Sections of a key-mask tile table for B batch elements and T tiles.
+struct TileTableLayout {
+  size_t prefix_off, list_off, bytes;
+};
+TileTableLayout tile_table_layout(int64_t B, int64_t T) {
+  TileTableLayout l;
+  l.prefix_off = align256(static_cast<size_t>(B * T) * sizeof(uint64_t));
+  l.list_off = l.prefix_off + align256(static_cast<size_t>(B * (T + 1)) * sizeof(int));
+  l.bytes = l.list_off + align256(static_cast<size_t>(B * T) * sizeof(int));
+  return l;
+}
+
+fa::MaskTiles mask_tiles_view(const void* tiles, int64_t B, int64_t H, int64_t N) {
+  const int64_t T = (N + 63) / 64;
+  const TileTableLayout l = tile_table_layout(B, T);
+  const char* base = static_cast<const char*>(tiles);
+  fa::MaskTiles m;
+  m.words = reinterpret_cast<const uint64_t*>(base);
+  m.prefix = reinterpret_cast<const int*>(base + l.prefix_off);
+  m.list = reinterpret_cast<const int*>(base + l.list_off);
+  m.n_tiles = static_cast<int>(T);
+  m.H = static_cast<int>(H);
+  return m;
+}
+
+fa::MaskTiles no_mask(int64_t H) {
+  fa::MaskTiles m;
+  m.words = nullptr;
+  m.prefix = nullptr;
+  m.list = nullptr;
+  m.n_tiles = 0;
+  m.H = static_cast<int>(H);
+  return m;
+}
+
+fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t N, float scale) {
+  fa::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.N = N;
+  a.BH = static_cast<int>(B * H);
+  a.n_qtiles = 0;  // set by the launcher from its tile shape
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.n_splits = 1;
+  a.part_lse = nullptr;
+  a.part_o = nullptr;
+  a.mask = no_mask(H);
+  return a;
+}
+
+fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, float scale, void* workspace) {
+  fa::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = static_cast<float*>(workspace);
+  a.N = N;
+  a.BH = static_cast<int>(B * H);
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.mask = no_mask(H);
+  return a;
+}
+
+// Checks shared by fa_bwd and fa_bwd_masked.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
+              int dtype, void* workspace, size_t workspace_bytes);
+
 }  // namespace
 
 extern "C" {
@@ -56,20 +136,42 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   int st = check_common(B, H, N, D, causal, scale, dtype);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
-  fa::FwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
-  a.N = N;
-  a.BH = static_cast<int>(B * H);
-  a.n_qtiles = 0;  // set by the launcher from its tile shape
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.n_splits = 1;
-  a.part_lse = nullptr;
-  a.part_o = nullptr;
+  const fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, scale);
   hipError_t e = fa::launch_fwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_mask_tiles_bytes(int64_t B, int64_t N) {
+  if (B <= 0 || N <= 0 || N > kMaxN) return 0;
+  const int64_t T = (N + 63) / 64;
+  if (B > kMaxWorkgroups / T) return 0;
+  return tile_table_layout(B, T).bytes;
+}
+
+int fa_mask_tiles(const uint8_t* key_mask, int64_t B, int64_t N, void* tiles, size_t tiles_bytes, void* stream) {
+  if (!key_mask) return FA_ERR_NULL;
+  if (B <= 0 || N <= 0 || N > kMaxN) return FA_ERR_SHAPE;
+  const size_t need = fa_mask_tiles_bytes(B, N);
+  if (need == 0) return FA_ERR_SHAPE;
+  if (!tiles || tiles_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(tiles)) return FA_ERR_ALIGN;
+  const fa::MaskTiles m = mask_tiles_view(tiles, B, 1, N);
+  hipError_t e = fa::launch_mask_tiles(key_mask, B, N, const_cast<uint64_t*>(m.words), const_cast<int*>(m.prefix),
+                                       const_cast<int*>(m.list), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles, void* stream) {
+  if (!q || !k || !v || !o || !lse || !tiles) return FA_ERR_NULL;
+  int st = check_common(B, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(tiles))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, scale);
+  a.mask = mask_tiles_view(tiles, B, H, N);
+  hipError_t e =
+      fa::launch_fwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -93,16 +195,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  fa::FwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
-  a.N = N;
-  a.BH = static_cast<int>(B * H);
-  a.n_qtiles = 0;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, scale);
   a.n_splits = num_splits;
   const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
   a.part_lse = static_cast<float*>(workspace);
@@ -121,6 +214,36 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int ca
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, workspace,
+                           workspace_bytes);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, scale, workspace);
+  hipError_t e = fa::launch_bwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
+                  int dtype, const void* tiles, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!tiles) return FA_ERR_NULL;
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, workspace,
+                           workspace_bytes);
+  if (st != FA_OK) return st;
+  if (!aligned16(tiles)) return FA_ERR_ALIGN;
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, scale, workspace);
+  a.mask = mask_tiles_view(tiles, B, H, N);
+  hipError_t e =
+      fa::launch_bwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
+              int dtype, void* workspace, size_t workspace_bytes) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_common(B, H, N, D, causal, scale, dtype);
   if (st != FA_OK) return st;
@@ -130,23 +253,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   const size_t need = fa_bwd_workspace_bytes(B, H, N, D, causal, dtype);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  fa::BwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<const uint16_t*>(o);
-  a.lse = lse;
-  a.dout = static_cast<const uint16_t*>(dout);
-  a.dq = static_cast<uint16_t*>(dq);
-  a.dk = static_cast<uint16_t*>(dk);
-  a.dv = static_cast<uint16_t*>(dv);
-  a.delta = static_cast<float*>(workspace);
-  a.N = N;
-  a.BH = static_cast<int>(B * H);
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = fa::launch_bwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return FA_OK;
 }
 
-}  // extern "C"
+}  // namespace

@@ -132,8 +132,13 @@ __device__ __forceinline__ int tr_offset(int r, int col) {
 // Query rows are read in perm23 order, so register r of lane-half g holds
 // query acc_row(r, g) of its 32-query block, and P / dS feed the next two
 // products straight from their accumulators.
+// MASK (key-padding mask): a hidden key has P = 0 in its whole column, so its
+// dK and dV rows are exactly zero and the visible keys' columns do not
+// depend on it (P uses the saved LSE).  Hidden keys are therefore computed
+// like the others and zeroed at the end; a wave whose 32 keys are all hidden
+// skips the products, and a workgroup with no visible key skips the loop.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, class T>
+template <int D, bool CAUSAL, class T, bool MASK>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = kTileRows;
   constexpr int RC = D / 8, TC = BQ * RC;
@@ -153,8 +158,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   const uint16_t* __restrict__ Gh = a.dout + head;
 
   const int k0w = kt * BK + wave * 32;
-  const bool active = k0w < N;
+  const bool in_range = k0w < N;
   const int my_k = k0w + l32;
+  // Mask mode: visibility words of the workgroup's two 64-key tiles; this
+  // wave's keys are half (wave % 2) of tile 2kt + wave / 2.
+  bool key_vis = true, wg_any = true;
+  uint32_t wave_bits = 0xffffffffu;
+  if constexpr (MASK) {
+    const int64_t b = bh / a.mask.H;
+    const uint64_t* wb = a.mask.words + b * a.mask.n_tiles;
+    const uint64_t w0 = wb[2 * kt];
+    const uint64_t w1 = 2 * kt + 1 < a.mask.n_tiles ? wb[2 * kt + 1] : 0;
+    wave_bits = (uint32_t)(((wave < 2) ? w0 : w1) >> ((wave & 1) * 32));
+    key_vis = ((wave_bits >> l32) & 1u) != 0;
+    wg_any = (w0 | w1) != 0;
+  }
+  const bool active = in_range && wave_bits != 0;
 
   // Resident B operands: lane (key, g) holds K[my_k][16c+8g..+8] and V
   // likewise; lanes past the last key re-read row N-1 and store nothing.
@@ -281,19 +300,27 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     if (qt + 1 < n_qt) put_rows(lln, ldn);
   };
 
-  if (qt_begin < n_qt) {
+  const int qt_end = wg_any ? n_qt : qt_begin;  // workgroup-uniform
+  if (qt_begin < qt_end) {
     const int valid = min(BQ, (int)N - qt_begin * BQ);
     copy_tile<D>(Qh + (int64_t)qt_begin * BQ * D, src0, lq0, wave, valid);
     copy_tile<D>(Gh + (int64_t)qt_begin * BQ * D, src0, lg0, wave, valid);
     fetch_rows(qt_begin);
     put_rows(ll0, ld0);
   }
-  for (int qt = qt_begin; qt < n_qt; qt += 2) {
+  for (int qt = qt_begin; qt < qt_end; qt += 2) {
     step(qt, lq0, lg0, ll0, ld0, lq1, lg1, ll1, ld1);
-    if (qt + 1 < n_qt) step(qt + 1, lq1, lg1, ll1, ld1, lq0, lg0, ll0, ld0);
+    if (qt + 1 < qt_end) step(qt + 1, lq1, lg1, ll1, ld1, lq0, lg0, ll0, ld0);
   }
 
-  if (!active || my_k >= N) return;
+  if (!in_range || my_k >= N) return;
+  if (MASK && !key_vis) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      dk[i] = f32x16{};
+      dv[i] = f32x16{};
+    }
+  }
   uint16_t* dk_row = a.dk + head + (int64_t)my_k * D;
   uint16_t* dv_row = a.dv + head + (int64_t)my_k * D;
   const float sc = a.scale;
@@ -317,8 +344,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
 //   dP^T = V dO^T       (A = V rows, B = dO^T)
 //   P^T  = exp2(S^T*scale*log2e - LSE*log2e), dS^T = P^T (dP^T - Delta)
 //   dQ^T += K^T dS^T    (A = K^T via transposed reads, B = dS^T)
+// MASK (key-padding mask): only the non-empty key tiles of the batch
+// element's list are visited, and hidden keys of partial tiles get P = 0.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, class T>
+template <int D, bool CAUSAL, class T, bool MASK>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   constexpr int BM = 128, BN = kTileRows;
   constexpr int RC = D / 8, TC = BN * RC;
@@ -382,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
   const float c2 = a.scale_log2;
 
-  auto compute = [&](int kt, const u32x4* Kl, const u32x4* Vl) {
+  auto compute = [&](int kt, uint32_t wlo, uint32_t whi, const u32x4* Kl, const u32x4* Vl) {
     const char* Kb = (const char*)Kl;
     const char* Vb = (const char*)Vl;
     const int k0 = kt * BN;
@@ -401,15 +430,18 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c2, -lse2));
-    // Diagonal tile or the partial last tile (keys >= N do not exist): zero
-    // the masked probabilities.  The test is uniform, so other tiles skip it.
-    if ((CAUSAL && k0 + BN - 1 > q0w) || k0 + BN > N) {
+    // Diagonal tile, partial last tile (keys >= N do not exist) or partially
+    // visible tile: zero the masked probabilities.  The test is uniform, so
+    // other tiles skip it.
+    const bool partial = MASK ? (wlo & whi) != 0xffffffffu : k0 + BN > N;
+    if ((CAUSAL && k0 + BN - 1 > q0w) || partial) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + acc_row(r, g);
-          if ((CAUSAL && key > my_q) || key >= N) s[kb][r] = 0.f;
+          const bool hidden = MASK ? key_hidden(wlo, whi, kb, r, g) : key >= N;
+          if ((CAUSAL && key > my_q) || hidden) s[kb][r] = 0.f;
         }
     }
 #pragma unroll
@@ -429,23 +461,63 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     }
   };
 
-  auto step = [&](int kt, const u32x4* Kl, const u32x4* Vl, u32x4* Kn, u32x4* Vn) {
-    wait_vmem();
-    __syncthreads();
-    if (kt + 1 < n_kt) {
-      const int valid = min(BN, (int)N - (kt + 1) * BN);
-      copy_tile<D>(Kh + (int64_t)(kt + 1) * BN * D, ksrc0, Kn, wave, valid);
-      copy_tile<D>(Vh + (int64_t)(kt + 1) * BN * D, vsrc0, Vn, wave, valid);
+  constexpr uint32_t kAll = 0xffffffffu;
+  if constexpr (!MASK) {
+    auto step = [&](int kt, const u32x4* Kl, const u32x4* Vl, u32x4* Kn, u32x4* Vn) {
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 < n_kt) {
+        const int valid = min(BN, (int)N - (kt + 1) * BN);
+        copy_tile<D>(Kh + (int64_t)(kt + 1) * BN * D, ksrc0, Kn, wave, valid);
+        copy_tile<D>(Vh + (int64_t)(kt + 1) * BN * D, vsrc0, Vn, wave, valid);
+      }
+      if (!active || (CAUSAL && kt * BN > q0w + 31)) return;
+      compute(kt, kAll, kAll, Kl, Vl);
+    };
+    copy_tile<D>(Kh, ksrc0, lk0, wave, min(BN, (int)N));
+    copy_tile<D>(Vh, vsrc0, lv0, wave, min(BN, (int)N));
+    for (int kt = 0; kt < n_kt; kt += 2) {
+      step(kt, lk0, lv0, lk1, lv1);
+      if (kt + 1 < n_kt) step(kt + 1, lk1, lv1, lk0, lv0);
     }
-    if (!active || (CAUSAL && kt * BN > q0w + 31)) return;
-    compute(kt, Kl, Vl);
-  };
-
-  copy_tile<D>(Kh, ksrc0, lk0, wave, min(BN, (int)N));
-  copy_tile<D>(Vh, vsrc0, lv0, wave, min(BN, (int)N));
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    step(kt, lk0, lv0, lk1, lv1);
-    if (kt + 1 < n_kt) step(kt + 1, lk1, lv1, lk0, lv0);
+  } else {
+    // The batch element's non-empty key tiles below the causal limit, at
+    // positions 0 .. i_end-1; position i is tile kt_c with word (w_lo, w_hi),
+    // and the copies started in its step are of the tile at position i+1.
+    const int64_t b = bh / a.mask.H;
+    const int i_end = a.mask.prefix[b * (a.mask.n_tiles + 1) + n_kt];
+    auto load = [&](int kt, u32x4* Kn, u32x4* Vn) {
+      const int valid = min(BN, (int)N - kt * BN);
+      copy_tile<D>(Kh + (int64_t)kt * BN * D, ksrc0, Kn, wave, valid);
+      copy_tile<D>(Vh + (int64_t)kt * BN * D, vsrc0, Vn, wave, valid);
+    };
+    if (i_end > 0) {  // workgroup-uniform
+      TileWindow win;
+      win.init(a.mask.list + b * a.mask.n_tiles, a.mask.words + b * a.mask.n_tiles, i_end, lane);
+      int kt_c = win.tile(0, lane);
+      uint32_t w_lo, w_hi;
+      win.word(0, w_lo, w_hi);
+      load(kt_c, lk0, lv0);
+      auto step = [&](int i, const u32x4* Kl, const u32x4* Vl, u32x4* Kn, u32x4* Vn) {
+        int kt1 = 0;
+        uint32_t lo1 = 0, hi1 = 0;
+        if (i + 1 < i_end) {
+          kt1 = win.tile(i + 1, lane);
+          win.word(i + 1, lo1, hi1);
+        }
+        wait_vmem();
+        __syncthreads();
+        if (i + 1 < i_end) load(kt1, Kn, Vn);
+        if (active && !(CAUSAL && kt_c * BN > q0w + 31)) compute(kt_c, w_lo, w_hi, Kl, Vl);
+        kt_c = kt1;
+        w_lo = lo1;
+        w_hi = hi1;
+      };
+      for (int i = 0; i < i_end; i += 2) {
+        step(i, lk0, lv0, lk1, lv1);
+        if (i + 1 < i_end) step(i + 1, lk1, lv1, lk0, lv0);
+      }
+    }
   }
 
   if (!active || !real_q) return;
@@ -460,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
                 pack2<T>(dq[db][rq * 4 + 2] * sc, dq[db][rq * 4 + 3] * sc)};
 }
 
-template <int D, bool CAUSAL, class T>
+template <int D, bool CAUSAL, class T, bool MASK>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.N;
   constexpr int rpb = kThreads / (D / 8);
@@ -469,12 +541,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n_ktiles = (a.N + 127) / 128;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, T>), dim3((unsigned)(a.BH * n_ktiles)), dim3(kThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(a.BH * n_ktiles)), dim3(kThreads), 0,
+                     stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n_qtiles = (a.N + 127) / 128;
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, T>), dim3((unsigned)(a.BH * n_qtiles)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(a.BH * n_qtiles)), dim3(kThreads), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
@@ -482,7 +555,22 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_BWD_CASE(DD, CC, TT) \
-  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT>(a, stream);
+  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, false>(a, stream);
+  FA_BWD_CASE(64, false, Fp16)
+  FA_BWD_CASE(64, true, Fp16)
+  FA_BWD_CASE(128, false, Fp16)
+  FA_BWD_CASE(128, true, Fp16)
+  FA_BWD_CASE(64, false, Bf16)
+  FA_BWD_CASE(64, true, Bf16)
+  FA_BWD_CASE(128, false, Bf16)
+  FA_BWD_CASE(128, true, Bf16)
+#undef FA_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_masked(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_BWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, true>(a, stream);
   FA_BWD_CASE(64, false, Fp16)
   FA_BWD_CASE(64, true, Fp16)
   FA_BWD_CASE(128, false, Fp16)

@@ -170,6 +170,54 @@ __device__ __forceinline__ void copy_tile_rows(const uint16_t* tile, int src0, u
                                              src0 * 2, i * NT * 16, 0, 0);
 }
 
+// The non-empty key tiles of a key-padding mask, as a workgroup walks them:
+// positions 0 .. end-1 of the batch element's compacted tile list.  A window
+// of 64 consecutive positions is held one per lane (tile index and the two
+// halves of its visibility word) and read with v_readlane, so a lookup costs
+// no memory access; positions must be looked up in increasing order, and the
+// window is refilled (one vector load per lane) once every 64 positions.
+struct TileWindow {
+  const int* list;
+  const uint64_t* words;
+  int end;
+  int base;
+  uint32_t t, lo, hi;
+
+  __device__ __forceinline__ void init(const int* list_b, const uint64_t* words_b, int n, int lane) {
+    list = list_b;
+    words = words_b;
+    end = n;
+    fill(0, lane);
+  }
+  __device__ __forceinline__ void fill(int b0, int lane) {
+    base = b0;
+    t = lo = hi = 0;
+    if (b0 + lane < end) {
+      const int tile = list[b0 + lane];
+      const uint64_t w = words[tile];
+      t = (uint32_t)tile;
+      lo = (uint32_t)w;
+      hi = (uint32_t)(w >> 32);
+    }
+  }
+  // Tile at position i (i < end) and its word; call tile(i) before word(i).
+  __device__ __forceinline__ int tile(int i, int lane) {
+    if (i - base >= 64) fill(i, lane);
+    return __builtin_amdgcn_readlane((int)t, i - base);
+  }
+  __device__ __forceinline__ void word(int i, uint32_t& wlo, uint32_t& whi) const {
+    wlo = (uint32_t)__builtin_amdgcn_readlane((int)lo, i - base);
+    whi = (uint32_t)__builtin_amdgcn_readlane((int)hi, i - base);
+  }
+};
+
+// True when key kb*32 + acc_row(r, g) of a 64-key tile is hidden by the
+// tile's visibility word (wlo: keys 0-31, whi: keys 32-63).
+__device__ __forceinline__ bool key_hidden(uint32_t wlo, uint32_t whi, int kb, int r, int g) {
+  const uint32_t wk = (kb ? whi : wlo) >> (8 * g);
+  return ((wk >> (16 * (r >> 3) + (r & 7))) & 1u) == 0;
+}
+
 // Wait until this wave's outstanding global loads (including LDS-bound ones)
 // have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -64,8 +64,13 @@ struct FwdShape {
 // SPLIT: the workgroup covers only key tiles [kt_begin, kt_end) of its split
 // and writes FP32 partial states (O normalised within the range, and the
 // range's LSE) for merge_kernel instead of the final O and LSE.
-template <int D, int QB, bool CAUSAL, class T, bool SPLIT>
+// MASK: a key-padding mask given by its block-level flags (a.mask): the
+// workgroup visits only the listed non-empty tiles, tests elements only in
+// tiles whose visibility word is not all ones, and a row left with no
+// visible key gets O = 0 and LSE = -inf.
+template <int D, int QB, bool CAUSAL, class T, bool SPLIT, bool MASK>
 __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdArgs a) {
+  static_assert(!(SPLIT && MASK), "split-K/V takes no mask");
   constexpr int BM = FwdShape<QB>::BM, BN = kFwdBN, NT = kFwdThreads;
   constexpr int RC = D / 8;              // 16-byte chunks per row
   constexpr int TC = BN * RC;            // chunks per K or V tile
@@ -118,9 +123,18 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
 
   const int n_kt_all = (int)((N + BN - 1) / BN);  // the last tile may be partial
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
-  // Key tiles of this workgroup: all visible ones, or this split's share.
-  const int kt_begin = SPLIT ? (int)(((int64_t)split * n_kt_all) / a.n_splits) : 0;
-  const int kt_end = SPLIT ? min(n_kt, (int)(((int64_t)(split + 1) * n_kt_all) / a.n_splits)) : n_kt;
+  // The workgroup walks positions i_begin .. i_end-1 of a tile sequence:
+  // without a mask position i is key tile i (all visible tiles, or this
+  // split's share); with a mask it is the i-th non-empty tile of the list,
+  // and the tiles before the causal limit n_kt are the first prefix[n_kt].
+  int i_begin = 0, i_end;
+  const int64_t b = MASK ? bh / a.mask.H : 0;  // batch element (mask mode only)
+  if constexpr (MASK) {
+    i_end = a.mask.prefix[b * (a.mask.n_tiles + 1) + n_kt];
+  } else {
+    i_begin = SPLIT ? (int)(((int64_t)split * n_kt_all) / a.n_splits) : 0;
+    i_end = SPLIT ? min(n_kt, (int)(((int64_t)(split + 1) * n_kt_all) / a.n_splits)) : n_kt;
+  }
 
   // Direct copies: copy i of wave w fills LDS chunks i*NT + 64w + lane.  The
   // per-lane source offsets (elements within a tile) differ between copies
@@ -162,35 +176,40 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   const int v_col = 16 * (vq & 1) + 4 * (vj & 3);
   const float c2 = a.scale_log2;
 
-  // One key tile kt, software-pipelined: on entry s holds the raw scores of
-  // tile kt (computed during the previous tile); while the softmax of tile
-  // kt runs on the vector ALUs, the score MFMAs of tile kt+1 (its K is
-  // already in LDS) are issued into s_nxt.  K therefore streams one tile
-  // ahead of V: the copies started here are K for tile kt+2 (into the buffer
-  // that held K of tile kt) and V for tile kt+1.
-  auto step = [&](int kt, const u32x4* __restrict__ Knext, const u32x4* __restrict__ Vcur, u32x4* kdst,
-                  u32x4* vdst, f32x16 (&s)[QB][2], f32x16 (&s_nxt)[QB][2]) {
-    wait_vmem();      // K of tile kt+1 and V of tile kt have landed (this wave's part)
-    __syncthreads();  // ... everyone's part; everyone is done with tile kt-1
-    if (kt + 2 < kt_end) load_k(kt + 2, kdst);
-    if (kt + 1 < kt_end) load_v(kt + 1, vdst);
+  // One position i of the tile sequence (key tile kt, its successors kt1
+  // and kt2 at positions i+1 and i+2), software-pipelined: on entry s holds
+  // the raw scores of tile kt (computed during the previous step); while the
+  // softmax of tile kt runs on the vector ALUs, the score MFMAs of tile kt1
+  // (its K is already in LDS) are issued into s_nxt.  K therefore streams
+  // one tile ahead of V: the copies started here are K of tile kt2 (into the
+  // buffer that held K of tile kt) and V of tile kt1.  wlo/whi: visibility
+  // word of tile kt (mask mode).
+  auto step = [&](int i, int kt, int kt1, int kt2, uint32_t wlo, uint32_t whi, const u32x4* __restrict__ Knext,
+                  const u32x4* __restrict__ Vcur, u32x4* kdst, u32x4* vdst, f32x16 (&s)[QB][2],
+                  f32x16 (&s_nxt)[QB][2]) {
+    wait_vmem();      // K of tile kt1 and V of tile kt have landed (this wave's part)
+    __syncthreads();  // ... everyone's part; everyone is done with the previous tile
+    if (i + 2 < i_end) load_k(kt2, kdst);
+    if (i + 1 < i_end) load_v(kt1, vdst);
 
     const int k0 = kt * BN;
     if (!active || (CAUSAL && k0 > q0w + WQ - 1)) return;  // nothing visible
 
-    // Diagonal tile, or the partial last tile: mask before the max (a block
-    // wholly above its queries is masked entirely and contributes zero
-    // probabilities; keys >= N do not exist).  Both tests are uniform, so
-    // full tiles below the diagonal take no per-element branch.
-    if ((CAUSAL && k0 + BN - 1 > q0w) || k0 + BN > N) {
+    // Diagonal tile, partial last tile or partially visible tile: mask
+    // before the max (a block wholly above its queries is masked entirely
+    // and contributes zero probabilities; keys >= N do not exist).  The
+    // tests are uniform, so other tiles take no per-element branch.
+    const bool partial = MASK ? (wlo & whi) != 0xffffffffu : k0 + BN > N;
+    if ((CAUSAL && k0 + BN - 1 > q0w) || partial) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + acc_row(r, g);
-            if ((CAUSAL && key > q0w + 32 * qb + ql) || key >= N) s[qb][kb][r] = -INFINITY;
+            const bool hidden = MASK ? key_hidden(wlo, whi, kb, r, g) : key >= N;
+            if ((CAUSAL && key > q0w + 32 * qb + ql) || hidden) s[qb][kb][r] = -INFINITY;
           }
     }
 
@@ -297,18 +316,59 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     }
   };
 
-  // Prologue: K and V of the first tile, K of the second, scores of the first.
+  // Prologue: K and V of the first tile, K of the second, scores of the
+  // first; then the steps, two per iteration so the LDS buffers alternate.
   f32x16 sA[QB][2], sB[QB][2];
-  if (kt_begin < kt_end) {  // workgroup-uniform
-    load_k(kt_begin, lds_k0);
-    load_v(kt_begin, lds_v0);
-    if (kt_begin + 1 < kt_end) load_k(kt_begin + 1, lds_k1);
+  if constexpr (!MASK) {
+    if (i_begin < i_end) {  // workgroup-uniform
+      load_k(i_begin, lds_k0);
+      load_v(i_begin, lds_v0);
+      if (i_begin + 1 < i_end) load_k(i_begin + 1, lds_k1);
+      wait_vmem();
+      __syncthreads();
+      if (active) scores(lds_k0, sA);
+      constexpr uint32_t kAll = 0xffffffffu;
+      for (int kt = i_begin; kt < i_end; kt += 2) {
+        step(kt, kt, kt + 1, kt + 2, kAll, kAll, lds_k1, lds_v0, lds_k0, lds_v1, sA, sB);
+        if (kt + 1 < i_end) step(kt + 1, kt + 1, kt + 2, kt + 3, kAll, kAll, lds_k0, lds_v1, lds_k1, lds_v0, sB, sA);
+      }
+    }
+  } else if (i_begin < i_end) {  // workgroup-uniform
+    TileWindow win;
+    win.init(a.mask.list + b * a.mask.n_tiles, a.mask.words + b * a.mask.n_tiles, i_end, lane);
+    // Tiles at positions i and i+1 (carried from step to step), their words.
+    int kt_c = win.tile(0, lane);
+    int kt_n = 1 < i_end ? win.tile(1, lane) : 0;
+    uint32_t w_lo, w_hi, wn_lo = 0, wn_hi = 0;
+    win.word(0, w_lo, w_hi);
+    if (1 < i_end) win.word(1, wn_lo, wn_hi);
+    load_k(kt_c, lds_k0);
+    load_v(kt_c, lds_v0);
+    if (i_begin + 1 < i_end) load_k(kt_n, lds_k1);
     wait_vmem();
     __syncthreads();
     if (active) scores(lds_k0, sA);
-    for (int kt = kt_begin; kt < kt_end; kt += 2) {
-      step(kt, lds_k1, lds_v0, lds_k0, lds_v1, sA, sB);
-      if (kt + 1 < kt_end) step(kt + 1, lds_k0, lds_v1, lds_k1, lds_v0, sB, sA);
+    // One position: the carried tiles advance by one and position i+2 is
+    // looked up first (before the step's wait, which any window refill shares).
+    auto run = [&](int i, const u32x4* Kn, const u32x4* Vc, u32x4* kd, u32x4* vd, f32x16 (&s)[QB][2],
+                   f32x16 (&sn)[QB][2]) {
+      int kt2 = 0;
+      uint32_t lo2 = 0, hi2 = 0;
+      if (i + 2 < i_end) {
+        kt2 = win.tile(i + 2, lane);
+        win.word(i + 2, lo2, hi2);
+      }
+      step(i, kt_c, kt_n, kt2, w_lo, w_hi, Kn, Vc, kd, vd, s, sn);
+      kt_c = kt_n;
+      kt_n = kt2;
+      w_lo = wn_lo;
+      w_hi = wn_hi;
+      wn_lo = lo2;
+      wn_hi = hi2;
+    };
+    for (int i = i_begin; i < i_end; i += 2) {
+      run(i, lds_k1, lds_v0, lds_k0, lds_v1, sA, sB);
+      if (i + 1 < i_end) run(i + 1, lds_k0, lds_v1, lds_k1, lds_v0, sB, sA);
     }
   }
 
@@ -343,7 +403,9 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   for (int qb = 0; qb < QB; ++qb) {
     const int my_q = q0w + 32 * qb + ql;
     const float l_tot = xhalf_sum(l_run[qb]);
-    const float inv = 1.f / l_tot;
+    // l_tot = 0 only for a row with no visible key (mask mode): O = 0, and
+    // the LSE below evaluates to -inf + -inf = -inf.
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (my_q >= N) continue;  // lanes past the last query
     uint16_t* Orow = a.o + head + (int64_t)my_q * D;
 #pragma unroll
@@ -397,7 +459,18 @@ hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+template <int D, int QB, bool CAUSAL, class T>
+hipError_t launch_fwd_masked_t(FwdArgs a, hipStream_t stream) {
+  constexpr int BM = FwdShape<QB>::BM;
+  a.n_qtiles = (int)((a.N + BM - 1) / BM);
+  const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
@@ -406,7 +479,8 @@ hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles * a.n_splits;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.BH * a.N;
@@ -421,6 +495,21 @@ hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_FWD_CASE(DD, CC, TT) \
   if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_t<DD, kFwdQB, CC, TT>(a, stream);
+  FA_FWD_CASE(64, false, Fp16)
+  FA_FWD_CASE(64, true, Fp16)
+  FA_FWD_CASE(128, false, Fp16)
+  FA_FWD_CASE(128, true, Fp16)
+  FA_FWD_CASE(64, false, Bf16)
+  FA_FWD_CASE(64, true, Bf16)
+  FA_FWD_CASE(128, false, Bf16)
+  FA_FWD_CASE(128, true, Bf16)
+#undef FA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_masked(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_FWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_masked_t<DD, kFwdQB, CC, TT>(a, stream);
   FA_FWD_CASE(64, false, Fp16)
   FA_FWD_CASE(64, true, Fp16)
   FA_FWD_CASE(128, false, Fp16)

@@ -6,6 +6,18 @@
 
 namespace fa {
 
+// Block-level flags of a key-padding mask, per batch element b and 64-key
+// tile t (built by launch_mask_tiles): words[b*T + t] has bit j set iff key
+// 64t + j exists and is visible; prefix[b*(T+1) + t] counts the non-empty
+// tiles before t; list[b*T + i] is the i-th non-empty tile.
+struct MaskTiles {
+  const uint64_t* words;
+  const int* prefix;
+  const int* list;
+  int n_tiles;  // T = ceil(N / 64)
+  int H;        // heads per batch element (bh / H = b)
+};
+
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -21,6 +33,7 @@ struct FwdArgs {
   int n_splits;
   float* part_lse;
   float* part_o;
+  MaskTiles mask;  // key-padding mask mode only
 };
 
 struct BwdArgs {
@@ -38,10 +51,16 @@ struct BwdArgs {
   int BH;
   float scale;       // the caller's scale (for dQ, dK)
   float scale_log2;  // scale * log2(e)
+  MaskTiles mask;    // key-padding mask mode only
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_fwd_masked(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_bwd_masked(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+// Builds the MaskTiles sections (words, prefix, list) from a [B, N] byte mask.
+hipError_t launch_mask_tiles(const uint8_t* key_mask, int64_t B, int64_t N, uint64_t* words, int* prefix, int* list,
+                             hipStream_t stream);
 
 }  // namespace fa

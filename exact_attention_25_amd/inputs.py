@@ -76,3 +76,36 @@ def make_inputs(B, H, N, D, dtype=FP16, seed=0, spiky_keys=False, with_dout=Fals
             x[..., ::64, :] *= np.float32(8.0)
         out[name] = x
     return out
+
+
+def make_key_mask(B, N, kind="lengths", seed=0, p=0.5, lengths=None):
+    """Seeded key-padding mask [B, N] (uint8, 1 = visible).
+
+    kinds:
+      "lengths" -- a right-padded variable-length batch: element b has
+                   ``lengths[b]`` real tokens (drawn uniformly in 1..N when
+                   not given), key j visible iff j < L_b;
+      "random"  -- every key visible with probability ``p`` (random mask
+                   patterns, which may leave rows with no visible key);
+      "blocks"  -- each 64-key tile is, with equal odds, wholly hidden,
+                   wholly visible or random with probability ``p``, so the
+                   block-level flags see every kind of tile;
+      "all"     -- every key visible.
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "lengths":
+        lens = np.asarray(lengths if lengths is not None else rng.integers(1, N + 1, size=B))
+        return (np.arange(N)[None, :] < lens[:, None]).astype(np.uint8)
+    if kind == "random":
+        return (rng.random((B, N)) < p).astype(np.uint8)
+    if kind == "blocks":
+        m = np.empty((B, N), dtype=np.uint8)
+        for b in range(B):
+            for t0 in range(0, N, 64):
+                c = rng.integers(0, 3)
+                n = min(64, N - t0)
+                m[b, t0:t0 + n] = 0 if c == 0 else (1 if c == 1 else (rng.random(n) < p))
+        return m
+    if kind == "all":
+        return np.ones((B, N), dtype=np.uint8)
+    raise ValueError("unknown mask kind %r" % kind)

@@ -150,6 +150,73 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int causal, float scale, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Key-padding masks (padded variable-length batches).
+ *
+ * A key-padding mask key_mask[B][N] (bytes, nonzero = visible) hides keys
+ * of batch element b from every query of b, in every head, like the causal
+ * mask: hidden scores are -inf before the row max.  A right-padded batch of
+ * sequences with lengths L_b is key_mask[b][j] = (j < L_b).  A row left
+ * with no visible key (possible with masks) gets O = 0 and LSE = -inf and
+ * contributes nothing to any gradient.
+ *
+ * Block-level flags ("FlashAttention dataflow and engineering validation on
+ * MI50", §4.3: on 64-wide waves the padding test belongs to the block loop,
+ * once per block, not to every element): fa_mask_tiles compresses the byte
+ * mask once into a tile table, which fa_fwd_masked and fa_bwd_masked read
+ * instead of the mask.  They visit only tiles with a visible key, and test
+ * elements only in tiles that are partly visible.
+ *
+ * Tile table (T = ceil(N/64); offsets from `tiles`, each section starting
+ * on a 256-byte boundary):
+ *   words  uint64 [B][T]    at 0: bit j of words[b][t] is set iff key
+ *                           64t + j exists (< N) and is visible;
+ *   prefix int32 [B][T+1]   at P = round_up(8*B*T, 256): number of tiles
+ *                           before t with a nonzero word;
+ *   list   int32 [B][T]     at P + round_up(4*B*(T+1), 256): list[b][i] is
+ *                           the i-th tile with a nonzero word, ascending
+ *                           (entries past prefix[b][T] unspecified).
+ * A table serves every call with the same B and N (all heads, fwd and bwd).
+ */
+
+/* fa_mask_tiles_bytes -- size of the tile table for B, N; 0 if B, N are
+ * out of range (B, N >= 1, N <= 2^30, B*ceil(N/64) < 2^31). */
+size_t fa_mask_tiles_bytes(int64_t B, int64_t N);
+
+/*
+ * fa_mask_tiles -- build the tile table of key_mask (device, [B][N] bytes,
+ * any alignment) into `tiles` (device, caller-owned, 16-byte aligned, at
+ * least fa_mask_tiles_bytes(B, N) bytes) on `stream`.  Two kernels: one
+ * wave per (b, tile) ballots the tile's 64 bytes into its word, then one
+ * workgroup per b scans the words into prefix and list.
+ * Errors: FA_ERR_NULL (key_mask), FA_ERR_SHAPE, FA_ERR_WORKSPACE (tiles
+ * missing or short), FA_ERR_ALIGN, FA_ERR_HIP.
+ */
+int fa_mask_tiles(const uint8_t* key_mask, int64_t B, int64_t N, void* tiles, size_t tiles_bytes, void* stream);
+
+/*
+ * fa_fwd_masked -- fa_fwd with a key-padding mask given by its tile table
+ * (built by fa_mask_tiles for the same B and N; its contents are trusted).
+ * Arguments, layouts and errors otherwise as for fa_fwd; FA_ERR_NULL for a
+ * NULL table.
+ */
+int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t H, int64_t N, int64_t D,
+                  int causal, float scale, int dtype, const void* tiles, void* stream);
+
+/*
+ * fa_bwd_masked -- fa_bwd for a forward computed by fa_fwd_masked with the
+ * same tile table.  Hidden keys get dK = dV = 0 exactly; rows without a
+ * visible key (LSE = -inf) get dQ = 0.  Arguments, workspace and errors as
+ * for fa_bwd; FA_ERR_NULL for a NULL table.
+ */
+int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv,
+                  int64_t B, int64_t H, int64_t N, int64_t D,
+                  int causal, float scale, int dtype, const void* tiles,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* fa_status_str -- a static, human-readable name for a status code. */
 const char* fa_status_str(int status);
 

@@ -24,8 +24,9 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_workspace_bytes", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_masked",
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles",
+                                    "fa_mask_tiles_bytes", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -116,3 +117,41 @@ def test_splitkv_workspace_bytes():
     assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 1) == 256 + 64 * 128 * 4
     assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 0) == 0
     assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 65) == 0
+
+
+def test_mask_tiles_bytes():
+    # T = 3 tiles: words 8*2*3 -> 256, prefix 4*2*4 -> 256, list 4*2*3 -> 256
+    assert fb.fa_mask_tiles_bytes(2, 130) == 768
+    assert fb.fa_mask_tiles_bytes(1, 64 * 100) == 1024 + 512 + 512
+    assert fb.fa_mask_tiles_bytes(0, 10) == 0 and fb.fa_mask_tiles_bytes(1, 0) == 0
+    assert fb.fa_mask_tiles_bytes(1, (1 << 30) + 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), 1), (dict(B=0), 2), (dict(N=0), 2), (dict(N=(1 << 30) + 1), 2),
+    (dict(tiles=None), 5), (dict(nb=767), 5), (dict(tiles=P + 8), 4),
+])
+def test_mask_tiles_rejects(kw, code):
+    a = dict(mask=P, B=2, N=130, tiles=P, nb=768)
+    a.update(kw)
+    assert fb.fa_mask_tiles(a["mask"], a["B"], a["N"], a["tiles"], a["nb"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 4), 4), (dict(q=None), 1),
+                                     (dict(D=80), 3), (dict(N=-1), 2), (dict(o=P + 2), 4)])
+def test_fwd_masked_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=128, D=64, causal=1, scale=0.125, dtype=0, tiles=P)
+    a.update(kw)
+    assert fb.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"],
+                            a["causal"], a["scale"], a["dtype"], a["tiles"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 4), 4), (dict(dk=None), 1),
+                                     (dict(ws=None), 5), (dict(dtype=3), 3)])
+def test_bwd_masked_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, N=128, D=64, causal=1,
+             scale=0.125, dtype=0, tiles=P, ws=P, wsb=1 << 20)
+    a.update(kw)
+    assert fb.fa_bwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                            a["B"], a["H"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"], a["tiles"],
+                            a["ws"], a["wsb"], None) == code

@@ -38,3 +38,17 @@ def test_spiky_rows():
     assert np.array_equal(b["k"][0, 0, rows % 64 == 0], 8 * a["k"][0, 0, rows % 64 == 0])
     assert np.array_equal(b["k"][0, 0, rows % 64 != 0], a["k"][0, 0, rows % 64 != 0])
     assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["v"], b["v"])
+
+
+def test_key_masks_are_seeded_and_shaped():
+    from exact_attention_25_amd.inputs import make_key_mask
+    for kind in ("lengths", "random", "blocks", "all"):
+        a = make_key_mask(3, 200, kind, seed=5)
+        b = make_key_mask(3, 200, kind, seed=5)
+        assert a.shape == (3, 200) and a.dtype == np.uint8 and np.array_equal(a, b)
+        assert set(np.unique(a)) <= {0, 1}
+    m = make_key_mask(2, 10, "lengths", lengths=[3, 10])
+    assert m.sum(axis=1).tolist() == [3, 10] and m[0, :3].all() and not m[0, 3:].any()
+    blk = make_key_mask(4, 640, "blocks", seed=1)
+    sums = blk.reshape(4, 10, 64).sum(axis=2)
+    assert (sums == 0).any() and (sums == 64).any() and ((sums > 0) & (sums < 64)).any()
