@@ -13,6 +13,11 @@ Conventions (shared with the C ABI only by *meaning*, not by code):
   aligned mask with -inf ([FA-CUDA] §1).
 * The log-sum-exp uses the natural logarithm: LSE_i = m_i + ln l_i
   ([FA-WHY] §3.2, last remark of the section).
+* Grouped heads: K and V may have H_kv heads with H_kv dividing the H query
+  heads (H_kv = 1: multi-query).  Query head h then reads K/V head
+  h // (H / H_kv) ("CUDA FlashAttention ...", §7 lists GQA/MQA among the
+  features a production kernel has to handle); the gradients of a shared
+  K/V head sum over the query heads of its group.
 * ``key_mask`` (optional, ``[B, N]``, nonzero = visible) is a key-padding
   mask: score S_ij of batch element b is -inf where key j is not visible,
   before the max, like the causal mask.  It is how padded variable-length
@@ -45,6 +50,14 @@ def _check4(*arrays):
     for a in arrays:
         if a.ndim != 4:
             raise ValueError("expected [B, H, N, D] arrays, got shape %r" % (a.shape,))
+
+
+def _group(q, k):
+    """Query heads per K/V head (H // H_kv); checks that H_kv divides H."""
+    H, Hkv = q.shape[1], k.shape[1]
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError("K/V heads (%d) must divide query heads (%d)" % (Hkv, H))
+    return H // Hkv
 
 
 # ---------------------------------------------------------------------------
@@ -111,6 +124,7 @@ def attention_forward(q, k, v, causal, scale, row_block=256, rows=None, key_mask
     q, k, v = _f64(q), _f64(k), _f64(v)
     _check4(q, k, v)
     B, H, N, D = q.shape
+    grp = _group(q, k)
     vis = _visibility(key_mask, B, N)
     sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = sel.shape[0]
@@ -118,7 +132,7 @@ def attention_forward(q, k, v, causal, scale, row_block=256, rows=None, key_mask
     lse = np.empty((B, H, R))
     for b in range(B):
         for h in range(H):
-            qh, kh, vh = q[b, h], k[b, h], v[b, h]
+            qh, kh, vh = q[b, h], k[b, h // grp], v[b, h // grp]
             for r0 in range(0, R, row_block):
                 r1 = min(R, r0 + row_block)
                 s, nk = _scores_block(qh, kh, 0, 0, causal, scale, rows=sel[r0:r1],
@@ -158,24 +172,26 @@ def attention_backward(q, k, v, do, causal, scale, row_block=256, key_mask=None)
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     _check4(q, k, v, do)
     B, H, N, D = q.shape
+    grp = _group(q, k)
     vis = _visibility(key_mask, B, N)
     dq = np.zeros((B, H, N, D))
-    dk = np.zeros((B, H, N, D))
-    dv = np.zeros((B, H, N, D))
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
     for b in range(B):
         for h in range(H):
-            qh, kh, vh, gh = q[b, h], k[b, h], v[b, h], do[b, h]
+            hk = h // grp  # the K/V head this query head reads; its gradients sum over the group
+            qh, kh, vh, gh = q[b, h], k[b, hk], v[b, hk], do[b, h]
             for i0 in range(0, N, row_block):
                 i1 = min(N, i0 + row_block)
                 s, nk = _scores_block(qh, kh, i0, i1, causal, scale, vis=None if vis is None else vis[b])
                 p, _, _ = _safe_softmax_rows(s)
                 g = gh[i0:i1]
-                dv[b, h, :nk] += p.T @ g
+                dv[b, hk, :nk] += p.T @ g
                 dp = g @ vh[:nk].T
                 delta = (p * dp).sum(axis=1)
                 ds = p * (dp - delta[:, None])
                 dq[b, h, i0:i1] = scale * (ds @ kh[:nk])
-                dk[b, h, :nk] += scale * (ds.T @ qh[i0:i1])
+                dk[b, hk, :nk] += scale * (ds.T @ qh[i0:i1])
     return dq, dk, dv
 
 

@@ -448,3 +448,63 @@ def test_key_tile_words_by_hand():
     m[1, 0] = m[1, 63] = m[1, 129] = 1
     words, tiles = key_tile_words(m)
     assert words == [[0, 2, 0], [1 | (1 << 63), 0, 0b10]] and tiles == [[1], [0, 2]]
+
+
+# --------------------------------------------------------------------------
+# Grouped K/V heads (GQA / MQA)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 1), (3, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_equal_repeated_kv(H, Hkv, causal):
+    n, d = 33, 8
+    q = _rand(500, 2, H, n, d)
+    k, v, do = _rand(501, 2, Hkv, n, d), _rand(502, 2, Hkv, n, d), _rand(503, 2, H, n, d)
+    rep = H // Hkv
+    k_rep, v_rep = np.repeat(k, rep, axis=1), np.repeat(v, rep, axis=1)
+    o, lse = attention_forward(q, k, v, causal, 0.3)
+    o2, lse2 = attention_forward(q, k_rep, v_rep, causal, 0.3)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    dq, dk, dv = attention_backward(q, k, v, do, causal, 0.3)
+    dq2, dk2, dv2 = attention_backward(q, k_rep, v_rep, do, causal, 0.3)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    assert np.abs(dq - dq2).max() < 1e-13
+    # a shared head's gradient is the sum over the query heads that read it
+    assert np.abs(dk - dk2.reshape(2, Hkv, rep, n, d).sum(axis=2)).max() < 1e-12
+    assert np.abs(dv - dv2.reshape(2, Hkv, rep, n, d).sum(axis=2)).max() < 1e-12
+
+
+def test_grouped_heads_brute_force():
+    n, d, H, Hkv = 5, 3, 4, 2
+    q, k, v = _rand(510, 1, H, n, d), _rand(511, 1, Hkv, n, d), _rand(512, 1, Hkv, n, d)
+    o, lse = attention_forward(q, k, v, True, 0.8)
+    for h in range(H):
+        ob, lb = brute_force_forward(q[0, h].tolist(), k[0, h * Hkv // H].tolist(), v[0, h * Hkv // H].tolist(),
+                                     True, 0.8)
+        assert np.abs(o[0, h] - np.array(ob)).max() < 1e-14 and np.abs(lse[0, h] - np.array(lb)).max() < 1e-14
+
+
+def test_grouped_heads_finite_differences():
+    n, d, H, Hkv = 6, 3, 4, 1
+    q, k, v = _rand(520, 1, H, n, d), _rand(521, 1, Hkv, n, d), _rand(522, 1, Hkv, n, d)
+    do = _rand(523, 1, H, n, d)
+    grads = attention_backward(q, k, v, do, True, 0.5)
+
+    def loss(q_, k_, v_):
+        return float((attention_forward(q_, k_, v_, True, 0.5)[0] * do).sum())
+
+    h = 1e-6
+    for gi, name in enumerate("qkv"):
+        base = [q, k, v]
+        num = np.zeros_like(base[gi])
+        for idx in np.ndindex(base[gi].shape):
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[gi][idx] += h
+            minus[gi][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        assert np.abs(num - grads[gi]).max() < 1e-8, name
+
+
+def test_grouped_heads_reject_non_divisor():
+    with pytest.raises(ValueError):
+        attention_forward(_rand(530, 1, 3, 4, 2), _rand(531, 1, 2, 4, 2), _rand(532, 1, 2, 4, 2), False, 1.0)
