@@ -51,6 +51,12 @@ def load_library():
     lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                            ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
     lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                               ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp]
+    lib.fa_fwd_gqa.restype = ctypes.c_int
+    lib.fa_bwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                               ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+    lib.fa_bwd_gqa.restype = ctypes.c_int
     lib.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
@@ -62,10 +68,10 @@ def load_library():
     lib.fa_mask_tiles_bytes.restype = ctypes.c_size_t
     lib.fa_mask_tiles.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_size_t, _vp]
     lib.fa_mask_tiles.restype = ctypes.c_int
-    lib.fa_fwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+    lib.fa_fwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, _vp]
     lib.fa_fwd_masked.restype = ctypes.c_int
-    lib.fa_bwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+    lib.fa_bwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, _vp, ctypes.c_size_t, _vp]
     lib.fa_bwd_masked.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
@@ -87,6 +93,17 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype,
            workspace, workspace_bytes, stream):
     return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, int(causal),
                                  float(scale), int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, stream):
+    return load_library().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale), int(dtype),
+                                     stream)
+
+
+def fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype,
+               workspace, workspace_bytes, stream):
+    return load_library().fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
+                                     float(scale), int(dtype), workspace, workspace_bytes, stream)
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, num_splits, workspace,
@@ -111,14 +128,14 @@ def fa_mask_tiles(key_mask, B, N, tiles, tiles_bytes, stream):
     return load_library().fa_mask_tiles(key_mask, B, N, tiles, tiles_bytes, stream)
 
 
-def fa_fwd_masked(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, tiles, stream):
-    return load_library().fa_fwd_masked(q, k, v, o, lse, B, H, N, D, int(causal), float(scale), int(dtype),
+def fa_fwd_masked(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, tiles, stream):
+    return load_library().fa_fwd_masked(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale), int(dtype),
                                         tiles, stream)
 
 
-def fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, tiles,
+def fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, tiles,
                   workspace, workspace_bytes, stream):
-    return load_library().fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, int(causal),
+    return load_library().fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
                                         float(scale), int(dtype), tiles, workspace, workspace_bytes, stream)
 
 
@@ -151,16 +168,28 @@ def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _kv_heads(q, k):
+    """H_kv from k's shape [B, H_kv, N, D] (grouped heads when H_kv < H)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, D] and [B, H_kv, N, D]")
+    B, H, N, D = q.shape
+    hkv = k.shape[1]
+    if hkv < 1 or H % hkv != 0:
+        raise ValueError("k has %d heads, which does not divide the %d query heads" % (hkv, H))
+    return hkv
+
+
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
-    """O, LSE = attention forward of [B, H, N, D] fp16/bf16 device tensors.
+    """O, LSE = attention forward of fp16/bf16 device tensors q [B, H, N, D]
+    and k, v [B, H_kv, N, D] (H_kv = H, or a divisor of H for grouped heads).
 
     Returns (o, lse) with o like q and lse float32 [B, H, N].
     """
     import torch
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, N, D]")
+    hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
-    _check({"q": q, "k": k, "v": v}, q.shape, q.dtype, q.device)
+    _check({"q": q}, q.shape, q.dtype, q.device)
+    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -169,10 +198,14 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check({"out": out}, q.shape, q.dtype, q.device)
     _check({"lse": lse}, (B, H, N), torch.float32, q.device)
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, H, N, D, causal, scale, _dtype_code(q), _stream_handle(q.device))
+    if hkv == H:
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, D, causal, scale, _dtype_code(q), _stream_handle(q.device))
+    else:
+        st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, hkv, N, D, causal, scale, _dtype_code(q), _stream_handle(q.device))
     if st != FA_OK:
-        raise FaError(st, "fa_fwd")
+        raise FaError(st, "fa_fwd" if hkv == H else "fa_fwd_gqa")
     return out, lse
 
 
@@ -203,10 +236,13 @@ def fwd_splitkv(q, k, v, num_splits, causal=False, scale=None, out=None, lse=Non
 
 
 def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
-    """dQ, dK, dV of the attention forward, by recomputation."""
+    """dQ, dK, dV of the attention forward, by recomputation (dK, dV shaped
+    like k, v: grouped heads get the sum over their query heads)."""
     import torch
+    hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
-    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
+    _check({"q": q, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
+    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
     _check({"lse": lse}, (B, H, N), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -214,12 +250,17 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
     need = bwd_workspace_bytes(B, H, N, D, causal, code)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, causal, scale, code,
-                workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    tail = (N, D, causal, scale, code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(q.device))
+    if hkv == H:
+        st = fa_bwd(*args, B, H, *tail)
+    else:
+        st = fa_bwd_gqa(*args, B, H, hkv, *tail)
     if st != FA_OK:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, "fa_bwd" if hkv == H else "fa_bwd_gqa")
     return dq, dk, dv
 
 
@@ -245,8 +286,10 @@ def fwd_masked(q, k, v, tiles, causal=False, scale=None, out=None, lse=None):
     """fa_fwd_masked with the tile table from mask_tiles().  Returns (o, lse);
     rows with no visible key get o = 0 and lse = -inf."""
     import torch
+    hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
-    _check({"q": q, "k": k, "v": v}, q.shape, q.dtype, q.device)
+    _check({"q": q}, q.shape, q.dtype, q.device)
+    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -258,7 +301,7 @@ def fwd_masked(q, k, v, tiles, causal=False, scale=None, out=None, lse=None):
     if tiles.numel() < fa_mask_tiles_bytes(B, N):
         raise ValueError("tile table too small for B=%d N=%d" % (B, N))
     st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                       B, H, N, D, causal, scale, _dtype_code(q), tiles.data_ptr(), _stream_handle(q.device))
+                       B, H, hkv, N, D, causal, scale, _dtype_code(q), tiles.data_ptr(), _stream_handle(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_fwd_masked")
     return out, lse
@@ -267,8 +310,10 @@ def fwd_masked(q, k, v, tiles, causal=False, scale=None, out=None, lse=None):
 def bwd_masked(q, k, v, o, lse, dout, tiles, causal=False, scale=None, workspace=None):
     """fa_bwd_masked: gradients of fwd_masked with the same tile table."""
     import torch
+    hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
-    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
+    _check({"q": q, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
+    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
     _check({"lse": lse}, (B, H, N), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -278,9 +323,9 @@ def bwd_masked(q, k, v, o, lse, dout, tiles, causal=False, scale=None, workspace
     need = bwd_workspace_bytes(B, H, N, D, causal, code)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     st = fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, causal, scale, code,
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, hkv, N, D, causal, scale, code,
                        tiles.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                        _stream_handle(q.device))
     if st != FA_OK:

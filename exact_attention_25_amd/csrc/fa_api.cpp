@@ -14,6 +14,7 @@ namespace {
 constexpr int64_t kMaxWorkgroups = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxN = int64_t(1) << 30;  // row indices inside a head are 32-bit in the kernels
 constexpr int kMaxSplits = 64;
+constexpr float kLog2e = 1.4426950408889634f;
 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
@@ -32,6 +33,12 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t D, int causal, float s
   return FA_OK;
 }
 
+// Grouped heads: H_kv K/V heads, each shared by H / H_kv query heads.
+int check_heads(int64_t H, int64_t H_kv) {
+  if (H_kv <= 0 || H_kv > H || H % H_kv != 0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 // Sections of a key-mask tile table for B batch elements and T tiles.
 struct TileTableLayout {
   size_t prefix_off, list_off, bytes;
@@ -44,7 +51,7 @@ TileTableLayout tile_table_layout(int64_t B, int64_t T) {
   return l;
 }
 
-fa::MaskTiles mask_tiles_view(const void* tiles, int64_t B, int64_t H, int64_t N) {
+fa::MaskTiles mask_tiles_view(const void* tiles, int64_t B, int64_t N) {
   const int64_t T = (N + 63) / 64;
   const TileTableLayout l = tile_table_layout(B, T);
   const char* base = static_cast<const char*>(tiles);
@@ -53,22 +60,20 @@ fa::MaskTiles mask_tiles_view(const void* tiles, int64_t B, int64_t H, int64_t N
   m.prefix = reinterpret_cast<const int*>(base + l.prefix_off);
   m.list = reinterpret_cast<const int*>(base + l.list_off);
   m.n_tiles = static_cast<int>(T);
-  m.H = static_cast<int>(H);
   return m;
 }
 
-fa::MaskTiles no_mask(int64_t H) {
+fa::MaskTiles no_mask() {
   fa::MaskTiles m;
   m.words = nullptr;
   m.prefix = nullptr;
   m.list = nullptr;
   m.n_tiles = 0;
-  m.H = static_cast<int>(H);
   return m;
 }
 
 fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                     int64_t N, float scale) {
+                     int64_t H_kv, int64_t N, float scale) {
   fa::FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -77,17 +82,20 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
   a.lse = lse;
   a.N = N;
   a.BH = static_cast<int>(B * H);
+  a.H = static_cast<int>(H);
+  a.Hkv = static_cast<int>(H_kv);
   a.n_qtiles = 0;  // set by the launcher from its tile shape
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * kLog2e;
   a.n_splits = 1;
   a.part_lse = nullptr;
   a.part_o = nullptr;
-  a.mask = no_mask(H);
+  a.mask = no_mask();
   return a;
 }
 
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, float scale, void* workspace) {
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, float scale,
+                     void* workspace) {
   fa::BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -101,16 +109,43 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
   a.delta = static_cast<float*>(workspace);
   a.N = N;
   a.BH = static_cast<int>(B * H);
+  a.H = static_cast<int>(H);
+  a.Hkv = static_cast<int>(H_kv);
   a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.mask = no_mask(H);
+  a.scale_log2 = scale * kLog2e;
+  a.mask = no_mask();
   return a;
 }
 
-// Checks shared by fa_bwd and fa_bwd_masked.
+int check_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t H_kv,
+              int64_t N, int64_t D, int causal, float scale, int dtype) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_heads(H, H_kv);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
-              int dtype, void* workspace, size_t workspace_bytes);
+              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, int causal,
+              float scale, int dtype, void* workspace, size_t workspace_bytes) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_heads(H, H_kv);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  const size_t need = align256(static_cast<size_t>(B * H * N) * sizeof(float));
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 }  // namespace
 
@@ -120,7 +155,8 @@ const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N is not positive, or the problem is too large";
+    case FA_ERR_SHAPE:
+      return "FA_ERR_SHAPE: B, H or N is not positive, H_kv does not divide H, or the problem is too large";
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: need D in {64,128}, dtype fp16/bf16, causal 0/1, finite scale > 0";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
@@ -130,16 +166,49 @@ const char* fa_status_str(int status) {
   }
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-           int64_t N, int64_t D, int causal, float scale, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  int st = check_common(B, H, N, D, causal, scale, dtype);
+// ---- forward ---------------------------------------------------------------
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+               int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
   if (st != FA_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
-  const fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, scale);
-  hipError_t e = fa::launch_fwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
+  return status_of(fa::launch_fwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
 }
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+           int64_t D, int causal, float scale, int dtype, void* stream) {
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype, stream);
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                                      int num_splits) {
+  if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK) return 0;
+  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
+  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
+  return align256(rows * sizeof(float)) + align256(rows * static_cast<size_t>(D) * sizeof(float));
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
+  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H, N, scale);
+  a.n_splits = num_splits;
+  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
+  a.part_lse = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
+  return status_of(
+      fa::launch_fwd_splitkv(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+}
+
+// ---- key-padding masks -----------------------------------------------------
 
 size_t fa_mask_tiles_bytes(int64_t B, int64_t N) {
   if (B <= 0 || N <= 0 || N > kMaxN) return 0;
@@ -155,105 +224,61 @@ int fa_mask_tiles(const uint8_t* key_mask, int64_t B, int64_t N, void* tiles, si
   if (need == 0) return FA_ERR_SHAPE;
   if (!tiles || tiles_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(tiles)) return FA_ERR_ALIGN;
-  const fa::MaskTiles m = mask_tiles_view(tiles, B, 1, N);
-  hipError_t e = fa::launch_mask_tiles(key_mask, B, N, const_cast<uint64_t*>(m.words), const_cast<int*>(m.prefix),
-                                       const_cast<int*>(m.list), static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const fa::MaskTiles m = mask_tiles_view(tiles, B, N);
+  return status_of(fa::launch_mask_tiles(key_mask, B, N, const_cast<uint64_t*>(m.words), const_cast<int*>(m.prefix),
+                                         const_cast<int*>(m.list), static_cast<hipStream_t>(stream)));
 }
 
 int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                  int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles, void* stream) {
-  if (!q || !k || !v || !o || !lse || !tiles) return FA_ERR_NULL;
-  int st = check_common(B, H, N, D, causal, scale, dtype);
+                  int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
+                  void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
   if (st != FA_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(tiles))
-    return FA_ERR_ALIGN;
-  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, scale);
-  a.mask = mask_tiles_view(tiles, B, H, N);
-  hipError_t e =
-      fa::launch_fwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  if (!tiles) return FA_ERR_NULL;
+  if (!aligned16(tiles)) return FA_ERR_ALIGN;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
+  a.mask = mask_tiles_view(tiles, B, N);
+  return status_of(
+      fa::launch_fwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
 }
 
-size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
-                                      int num_splits) {
-  if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK) return 0;
-  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
-  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
-  return align256(rows * sizeof(float)) + align256(rows * static_cast<size_t>(D) * sizeof(float));
-}
-
-int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                   int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  int st = check_common(B, H, N, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
-  if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
-  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, scale);
-  a.n_splits = num_splits;
-  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
-  a.part_lse = static_cast<float*>(workspace);
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
-  hipError_t e =
-      fa::launch_fwd_splitkv(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
+// ---- backward --------------------------------------------------------------
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype) {
   if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK) return 0;
-  const size_t bytes = static_cast<size_t>(B * H * N) * sizeof(float);
-  return (bytes + 255) & ~static_cast<size_t>(255);
+  return align256(static_cast<size_t>(B * H * N) * sizeof(float));
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, int causal,
+               float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
+                           workspace_bytes);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, scale, workspace);
+  return status_of(fa::launch_bwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, workspace,
-                           workspace_bytes);
-  if (st != FA_OK) return st;
-  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, scale, workspace);
-  hipError_t e = fa::launch_bwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, D, causal, scale, dtype, workspace,
+                    workspace_bytes, stream);
 }
 
 int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                  void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
-                  int dtype, const void* tiles, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!tiles) return FA_ERR_NULL;
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, workspace,
+                  void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                  int causal, float scale, int dtype, const void* tiles, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
                            workspace_bytes);
   if (st != FA_OK) return st;
+  if (!tiles) return FA_ERR_NULL;
   if (!aligned16(tiles)) return FA_ERR_ALIGN;
-  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, scale, workspace);
-  a.mask = mask_tiles_view(tiles, B, H, N);
-  hipError_t e =
-      fa::launch_bwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, scale, workspace);
+  a.mask = mask_tiles_view(tiles, B, N);
+  return status_of(
+      fa::launch_bwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
-
-namespace {
-
-int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
-              int dtype, void* workspace, size_t workspace_bytes) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-  int st = check_common(B, H, N, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FA_ERR_ALIGN;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N, D, causal, dtype);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  return FA_OK;
-}
-
-}  // namespace

@@ -121,9 +121,12 @@ __device__ __forceinline__ int tr_offset(int r, int col) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 128 keys of one head; wave w owns keys k0w .. k0w+31.
-// K and V rows stay in VGPRs as B operands; tiles of 64 queries of Q and dO
-// (plus their LSE and Delta) stream through a double-buffered LDS ring.
+// dK, dV: workgroup = 128 keys of one K/V head; wave w owns keys k0w ..
+// k0w+31.  K and V rows stay in VGPRs as B operands; tiles of 64 queries of
+// Q and dO (plus their LSE and Delta) stream through a double-buffered LDS
+// ring -- for grouped heads, the tiles of every query head that shares this
+// K/V head, one head after the other, so dK and dV sum over the group in
+// registers.
 //   S    = Q K^T        (A = Q rows,  B = K^T)        queries x keys
 //   dP   = dO V^T       (A = dO rows, B = V^T)
 //   P    = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - Delta)
@@ -150,12 +153,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int64_t N = a.N;
-  const int bh = blockIdx.x % a.BH;
-  const int kt = blockIdx.x / a.BH;  // key tiles heaviest (lowest) first
-  const int64_t head = (int64_t)bh * N * D;
-  const int64_t rowbase = (int64_t)bh * N;
-  const uint16_t* __restrict__ Qh = a.q + head;
-  const uint16_t* __restrict__ Gh = a.dout + head;
+  const int G = a.H / a.Hkv;              // query heads per K/V head
+  const int BHkv = a.BH / G;
+  const int bhk = blockIdx.x % BHkv;       // K/V head; its query heads are bhk*G .. bhk*G+G-1
+  const int kt = blockIdx.x / BHkv;        // key tiles heaviest (lowest) first
+  const int64_t head = (int64_t)bhk * N * D;
 
   const int k0w = kt * BK + wave * 32;
   const bool in_range = k0w < N;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   bool key_vis = true, wg_any = true;
   uint32_t wave_bits = 0xffffffffu;
   if constexpr (MASK) {
-    const int64_t b = bh / a.mask.H;
+    const int64_t b = bhk / a.Hkv;
     const uint64_t* wb = a.mask.words + b * a.mask.n_tiles;
     const uint64_t w0 = wb[2 * kt];
     const uint64_t w1 = 2 * kt + 1 < a.mask.n_tiles ? wb[2 * kt + 1] : 0;
@@ -216,8 +218,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   // threads 0..63 and are written to LDS at the end of a step.  Rows past the
   // last query get an offset of +inf, hence P = 0 and dS = 0.
   float lse_n = 0.f, dl_n = 0.f;
-  auto fetch_rows = [&](int qt) {
+  auto fetch_rows = [&](int j, int qt) {  // query head bhk*G + j, tile qt
     if (tid < BQ) {
+      const int64_t rowbase = (int64_t)(bhk * G + j) * N;
       const int row = qt * BQ + tid;
       lse_n = row < N ? lse_offset(a.lse[rowbase + row]) : INFINITY;
       dl_n = row < N ? a.delta[rowbase + row] : 0.f;
@@ -286,31 +289,55 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     }
   };
 
-  auto step = [&](int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld, u32x4* Qn,
-                  u32x4* Gn, float* lln, float* ldn) {
-    wait_vmem();      // this wave's copies of tile qt have landed
-    __syncthreads();  // everyone's have (and the LSE/Delta rows); tile qt-1 is done
-    if (qt + 1 < n_qt) {
-      fetch_rows(qt + 1);  // first, so that storing them later need not wait for the tile copies
-      const int valid = min(BQ, (int)N - (qt + 1) * BQ);
-      copy_tile<D>(Qh + (int64_t)(qt + 1) * BQ * D, src0, Qn, wave, valid);
-      copy_tile<D>(Gh + (int64_t)(qt + 1) * BQ * D, src0, Gn, wave, valid);
+  // The workgroup walks positions p = 0 .. n_pos-1, position p being query
+  // tile qt of query head bhk*G + j (j-major: all tiles of a head, then the
+  // next head).  A step computes its tile and starts the copies of the next
+  // position's tile (jn, qtn) into the other buffers.
+  const int qt_end = wg_any ? n_qt : qt_begin;  // workgroup-uniform
+  const int nq = qt_end - qt_begin;
+  const int n_pos = G * nq;
+  auto load = [&](int j, int qt, u32x4* Qn, u32x4* Gn) {
+    const int64_t off = (int64_t)(bhk * G + j) * N * D + (int64_t)qt * BQ * D;
+    const int valid = min(BQ, (int)N - qt * BQ);
+    copy_tile<D>(a.q + off, src0, Qn, wave, valid);
+    copy_tile<D>(a.dout + off, src0, Gn, wave, valid);
+  };
+  auto step = [&](int p, int qt, int jn, int qtn, const u32x4* Ql, const u32x4* Gl, const float* ll,
+                  const float* ld, u32x4* Qn, u32x4* Gn, float* lln, float* ldn) {
+    wait_vmem();      // this wave's copies of position p have landed
+    __syncthreads();  // everyone's have (and the LSE/Delta rows); position p-1 is done
+    if (p + 1 < n_pos) {
+      fetch_rows(jn, qtn);  // first, so that storing them later need not wait for the tile copies
+      load(jn, qtn, Qn, Gn);
     }
     if (active) compute(qt, Ql, Gl, ll, ld);
-    if (qt + 1 < n_qt) put_rows(lln, ldn);
+    if (p + 1 < n_pos) put_rows(lln, ldn);
+  };
+  // (j, qt) -> the next position
+  auto advance = [&](int& j, int& qt) {
+    if (++qt == qt_end) {
+      qt = qt_begin;
+      ++j;
+    }
   };
 
-  const int qt_end = wg_any ? n_qt : qt_begin;  // workgroup-uniform
-  if (qt_begin < qt_end) {
-    const int valid = min(BQ, (int)N - qt_begin * BQ);
-    copy_tile<D>(Qh + (int64_t)qt_begin * BQ * D, src0, lq0, wave, valid);
-    copy_tile<D>(Gh + (int64_t)qt_begin * BQ * D, src0, lg0, wave, valid);
-    fetch_rows(qt_begin);
+  if (n_pos > 0) {
+    load(0, qt_begin, lq0, lg0);
+    fetch_rows(0, qt_begin);
     put_rows(ll0, ld0);
   }
-  for (int qt = qt_begin; qt < qt_end; qt += 2) {
-    step(qt, lq0, lg0, ll0, ld0, lq1, lg1, ll1, ld1);
-    if (qt + 1 < qt_end) step(qt + 1, lq1, lg1, ll1, ld1, lq0, lg0, ll0, ld0);
+  int j_c = 0, qt_c = qt_begin;
+  for (int p = 0; p < n_pos; p += 2) {
+    int j1 = j_c, qt1 = qt_c;
+    advance(j1, qt1);
+    step(p, qt_c, j1, qt1, lq0, lg0, ll0, ld0, lq1, lg1, ll1, ld1);
+    if (p + 1 < n_pos) {
+      int j2 = j1, qt2 = qt1;
+      advance(j2, qt2);
+      step(p + 1, qt1, j2, qt2, lq1, lg1, ll1, ld1, lq0, lg0, ll0, ld0);
+      j_c = j2;
+      qt_c = qt2;
+    }
   }
 
   if (!in_range || my_k >= N) return;
@@ -337,7 +364,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup = 128 queries of one head; wave w owns queries q0w .. q0w+31.
+// dQ: workgroup = 128 queries of one query head (its K/V from the head it
+// shares); wave w owns queries q0w .. q0w+31.
 // Q and dO rows stay in VGPRs as B operands; tiles of 64 keys of K and V
 // stream through a double-buffered LDS ring.
 //   S^T  = K Q^T        (A = K rows, B = Q^T)         keys x queries
@@ -359,12 +387,14 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const int ql = lane & 31, g = lane >> 5;
   const int64_t N = a.N;
   const int n_qtiles = (int)((N + BM - 1) / BM);
-  const int bh = blockIdx.x % a.BH;
+  const int G = a.H / a.Hkv;  // query heads per K/V head
+  const int bh = head_of_slot(blockIdx.x % a.BH, a.BH, G);
   const int rank = blockIdx.x / a.BH;
   const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
   const int64_t head = (int64_t)bh * N * D;
-  const uint16_t* __restrict__ Kh = a.k + head;
-  const uint16_t* __restrict__ Vh = a.v + head;
+  const int64_t kv_head = (int64_t)(bh / G) * N * D;
+  const uint16_t* __restrict__ Kh = a.k + kv_head;
+  const uint16_t* __restrict__ Vh = a.v + kv_head;
 
   const int q0w = qt * BM + wave * 32;
   const bool active = q0w < N;
@@ -484,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     // The batch element's non-empty key tiles below the causal limit, at
     // positions 0 .. i_end-1; position i is tile kt_c with word (w_lo, w_hi),
     // and the copies started in its step are of the tile at position i+1.
-    const int64_t b = bh / a.mask.H;
+    const int64_t b = bh / a.H;
     const int i_end = a.mask.prefix[b * (a.mask.n_tiles + 1) + n_kt];
     auto load = [&](int kt, u32x4* Kn, u32x4* Vn) {
       const int valid = min(BN, (int)N - kt * BN);
@@ -541,7 +571,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n_ktiles = (a.N + 127) / 128;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(a.BH * n_ktiles)), dim3(kThreads), 0,
+  const int64_t n_kv_heads = a.BH / (a.H / a.Hkv);
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(n_kv_heads * n_ktiles)), dim3(kThreads), 0,
                      stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -10,6 +10,10 @@
 // ...", §6).  Tiles wholly above the causal diagonal are never visited
 // ("Why FlashAttention does not need to store the attention matrix", §4.5).
 //
+// Grouped heads (GQA/MQA): a query head reads the K/V head of its group in
+// place, never a copy ("CUDA FlashAttention ...", §7), and the workgroups of
+// one group are numbered so that they share an XCD (head_of_slot).
+//
 // Work decomposition (one workgroup = 4 waves of one head):
 //  * Each wave owns QB blocks of 32 queries (QB = 1 or 2).  Their Q rows stay
 //    in VGPRs for the whole pass as the B operand of S^T = K Q^T (32 keys x
@@ -88,14 +92,16 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   const int ql = lane & 31, g = lane >> 5;
 
   const int64_t N = a.N;
-  const int bh = blockIdx.x % a.BH;
+  const int G = a.H / a.Hkv;  // query heads per K/V head
+  const int bh = head_of_slot(blockIdx.x % a.BH, a.BH, G);
   const int split = SPLIT ? (blockIdx.x / a.BH) % a.n_splits : 0;
   const int rank = SPLIT ? blockIdx.x / (a.BH * a.n_splits) : blockIdx.x / a.BH;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - rank) : rank;
   const int64_t head = (int64_t)bh * N * D;
+  const int64_t kv_head = (int64_t)(bh / G) * N * D;  // the K/V head this query head reads
   const uint16_t* __restrict__ Qh = a.q + head;
-  const uint16_t* __restrict__ Kh = a.k + head;
-  const uint16_t* __restrict__ Vh = a.v + head;
+  const uint16_t* __restrict__ Kh = a.k + kv_head;
+  const uint16_t* __restrict__ Vh = a.v + kv_head;
 
   const int q0w = qt * BM + wave * WQ;  // first query of this wave
   const bool active = q0w < N;          // the wave has at least one real query
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   // split's share); with a mask it is the i-th non-empty tile of the list,
   // and the tiles before the causal limit n_kt are the first prefix[n_kt].
   int i_begin = 0, i_end;
-  const int64_t b = MASK ? bh / a.mask.H : 0;  // batch element (mask mode only)
+  const int64_t b = MASK ? bh / a.H : 0;  // batch element (mask mode only)
   if constexpr (MASK) {
     i_end = a.mask.prefix[b * (a.mask.n_tiles + 1) + n_kt];
   } else {

@@ -15,8 +15,17 @@ struct MaskTiles {
   const int* prefix;
   const int* list;
   int n_tiles;  // T = ceil(N / 64)
-  int H;        // heads per batch element (bh / H = b)
 };
+
+// Grouped heads: query head bh = b*H + h reads K/V head b*Hkv + h/G, with
+// G = H / Hkv, i.e. K/V head bh / G.  Kernels number the query heads of a
+// launch so that the G heads sharing K/V are NG = B*Hkv apart: slot s is
+// query head (s % NG) * G + s / NG (the identity when G = 1).  With NG a
+// multiple of 8 every group then lands on one XCD and shares its L2.
+__host__ __device__ inline int head_of_slot(int s, int BH, int G) {
+  const int NG = BH / G;
+  return (s % NG) * G + s / NG;
+}
 
 struct FwdArgs {
   const uint16_t* q;
@@ -25,7 +34,8 @@ struct FwdArgs {
   uint16_t* o;
   float* lse;
   int64_t N;
-  int BH;          // B * H
+  int BH;          // B * H (query heads)
+  int H, Hkv;      // query heads and K/V heads per batch element; Hkv divides H
   int n_qtiles;    // ceil(N / queries per workgroup), filled in by the launcher
   float scale_log2;  // scale * log2(e)
   // Split-K/V mode only: number of key ranges and the FP32 partial states,
@@ -48,7 +58,8 @@ struct BwdArgs {
   uint16_t* dv;
   float* delta;      // workspace: [B*H*N] FP32
   int64_t N;
-  int BH;
+  int BH;            // B * H (query heads)
+  int H, Hkv;        // query heads and K/V heads per batch element; Hkv divides H
   float scale;       // the caller's scale (for dQ, dK)
   float scale_log2;  // scale * log2(e)
   MaskTiles mask;    // key-padding mask mode only

@@ -62,7 +62,8 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
-  FA_ERR_SHAPE = 2,       /* B, H or N <= 0, N > 2^30, or the grid is too large   */
+  FA_ERR_SHAPE = 2,       /* B, H or N <= 0, N > 2^30, H_kv not dividing H, or
+                             the grid is too large                              */
   FA_ERR_UNSUPPORTED = 3, /* D, dtype, causal flag or scale unsupported          */
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
   FA_ERR_WORKSPACE = 5,   /* backward workspace missing or smaller than needed   */
@@ -86,6 +87,21 @@ typedef enum fa_dtype { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t H, int64_t N, int64_t D,
            int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_gqa -- fa_fwd with grouped K/V heads (GQA; H_kv = 1 is MQA).
+ *   q, o : [B, H, N, D];  k, v : [B, H_kv, N, D];  lse : FP32 [B, H, N].
+ *   H_kv must divide H; query head h of batch element b reads K/V head
+ *   h / (H / H_kv) of b in place -- no copy of K or V is made ("CUDA
+ *   FlashAttention ...", §7: query heads map onto a shared K/V head, and
+ *   their reuse is planned with the workgroup schedule: the workgroups of
+ *   one group are numbered onto the same XCD when B*H_kv is a multiple of 8).
+ * fa_fwd(...) is fa_fwd_gqa(..., H, H, ...).  Errors as for fa_fwd, plus
+ * FA_ERR_SHAPE when H_kv < 1 or H_kv does not divide H.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+               int causal, float scale, int dtype, void* stream);
 
 /*
  * fa_fwd_splitkv_workspace_bytes -- bytes of device workspace fa_fwd_splitkv
@@ -151,6 +167,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_bwd_gqa -- fa_bwd for a forward computed by fa_fwd_gqa.
+ *   dk, dv : [B, H_kv, N, D]; every other tensor as in fa_fwd_gqa / fa_bwd.
+ * The gradient of a shared K/V head is the sum over the H / H_kv query heads
+ * that read it, accumulated in FP32 registers by one workgroup per 128 keys
+ * (it walks the query tiles of every head of the group), so the result is
+ * still bitwise reproducible.  Workspace: fa_bwd_workspace_bytes(B, H, ...).
+ */
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout,
+               void* dq, void* dk, void* dv,
+               int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+               int causal, float scale, int dtype,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Key-padding masks (padded variable-length batches).
  *
  * A key-padding mask key_mask[B][N] (bytes, nonzero = visible) hides keys
@@ -195,25 +226,26 @@ size_t fa_mask_tiles_bytes(int64_t B, int64_t N);
 int fa_mask_tiles(const uint8_t* key_mask, int64_t B, int64_t N, void* tiles, size_t tiles_bytes, void* stream);
 
 /*
- * fa_fwd_masked -- fa_fwd with a key-padding mask given by its tile table
- * (built by fa_mask_tiles for the same B and N; its contents are trusted).
- * Arguments, layouts and errors otherwise as for fa_fwd; FA_ERR_NULL for a
- * NULL table.
+ * fa_fwd_masked -- fa_fwd_gqa with a key-padding mask given by its tile
+ * table (built by fa_mask_tiles for the same B and N; its contents are
+ * trusted).  Arguments, layouts and errors otherwise as for fa_fwd_gqa
+ * (pass H_kv = H for plain multi-head attention); FA_ERR_NULL for a NULL
+ * table.
  */
 int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
-                  int64_t B, int64_t H, int64_t N, int64_t D,
+                  int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
                   int causal, float scale, int dtype, const void* tiles, void* stream);
 
 /*
- * fa_bwd_masked -- fa_bwd for a forward computed by fa_fwd_masked with the
- * same tile table.  Hidden keys get dK = dV = 0 exactly; rows without a
+ * fa_bwd_masked -- fa_bwd_gqa for a forward computed by fa_fwd_masked with
+ * the same tile table.  Hidden keys get dK = dV = 0 exactly; rows without a
  * visible key (LSE = -inf) get dQ = 0.  Arguments, workspace and errors as
- * for fa_bwd; FA_ERR_NULL for a NULL table.
+ * for fa_bwd_gqa; FA_ERR_NULL for a NULL table.
  */
 int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dout,
                   void* dq, void* dk, void* dv,
-                  int64_t B, int64_t H, int64_t N, int64_t D,
+                  int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
                   int causal, float scale, int dtype, const void* tiles,
                   void* workspace, size_t workspace_bytes, void* stream);
 

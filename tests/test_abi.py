@@ -24,9 +24,10 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_masked",
-                                    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles",
-                                    "fa_mask_tiles_bytes", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_gqa", "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_fwd",
+                                    "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_splitkv",
+                                    "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
+                                    "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -138,20 +139,41 @@ def test_mask_tiles_rejects(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 4), 4), (dict(q=None), 1),
-                                     (dict(D=80), 3), (dict(N=-1), 2), (dict(o=P + 2), 4)])
+                                     (dict(D=80), 3), (dict(N=-1), 2), (dict(o=P + 2), 4), (dict(Hkv=3), 2),
+                                     (dict(Hkv=0), 2)])
 def test_fwd_masked_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=128, D=64, causal=1, scale=0.125, dtype=0, tiles=P)
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Hkv=2, N=128, D=64, causal=1, scale=0.125, dtype=0, tiles=P)
     a.update(kw)
-    assert fb.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"],
+    assert fb.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["D"],
                             a["causal"], a["scale"], a["dtype"], a["tiles"], None) == code
 
 
 @pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 4), 4), (dict(dk=None), 1),
                                      (dict(ws=None), 5), (dict(dtype=3), 3)])
 def test_bwd_masked_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, N=128, D=64, causal=1,
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, Hkv=1, N=128, D=64, causal=1,
              scale=0.125, dtype=0, tiles=P, ws=P, wsb=1 << 20)
     a.update(kw)
     assert fb.fa_bwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
-                            a["B"], a["H"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"], a["tiles"],
-                            a["ws"], a["wsb"], None) == code
+                            a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"],
+                            a["tiles"], a["ws"], a["wsb"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(Hkv=0), 2), (dict(Hkv=3), 2), (dict(Hkv=5), 2), (dict(H=0), 2),
+                                     (dict(k=None), 1), (dict(v=P + 2), 4), (dict(D=32), 3)])
+def test_fwd_gqa_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=128, D=64, causal=1, scale=0.125, dtype=0)
+    a.update(kw)
+    assert fb.fa_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["D"],
+                         a["causal"], a["scale"], a["dtype"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(Hkv=3), 2), (dict(dv=None), 1), (dict(ws=None), 5),
+                                     (dict(wsb=4 * 4 * 128 - 1), 5)])
+def test_bwd_gqa_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=4, Hkv=1, N=128, D=64, causal=0,
+             scale=0.125, dtype=1, ws=P, wsb=1 << 20)
+    a.update(kw)
+    assert fb.fa_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                         a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"],
+                         a["ws"], a["wsb"], None) == code
