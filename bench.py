@@ -20,6 +20,7 @@ rocprofv3 FETCH_SIZE / WRITE_SIZE counters can be calibrated against a
 kernel whose HBM traffic is known.
 --mode fwd-only / bwd-only launch just that pass K times (for profiling).
 --splits S times fa_fwd_splitkv with S key splits instead of fa_fwd.
+--kv-heads G gives K and V only G heads (grouped-query attention).
 --mask KIND times fa_fwd_masked / fa_bwd_masked with a seeded key-padding
 mask (lengths / random / blocks / all); TFLOP/s then count only the visible
 (query, key) pairs, and the one-off tile-table build is reported apart.
@@ -60,6 +61,8 @@ def parse():
     p.add_argument("--mode", default="bench", choices=["bench", "copy", "fwd-only", "bwd-only"])
     p.add_argument("--splits", type=int, default=0,
                    help="time fa_fwd_splitkv with this many key splits (split pass + merge) instead of fa_fwd")
+    p.add_argument("--kv-heads", type=int, default=0,
+                   help="grouped heads: K and V get this many heads (must divide H); 0 = H")
     p.add_argument("--mask", default=None, choices=["lengths", "random", "blocks", "all"],
                    help="time fa_fwd_masked / fa_bwd_masked with a seeded key-padding mask of this kind; "
                         "FLOPs then count only visible (query, key) pairs")
@@ -157,6 +160,11 @@ def main():
     inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys, with_dout=True)
     q, k, v, do = (torch.from_numpy(inp[n]).to(dev).to(tdt).contiguous() for n in ("q", "k", "v", "do"))
     del inp
+    hkv = args.kv_heads or w.H
+    if w.H % hkv:
+        sys.exit("--kv-heads %d does not divide H=%d" % (hkv, w.H))
+    if hkv != w.H:  # the first hkv heads of the drawn K and V serve as the shared heads
+        k, v = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -232,7 +240,7 @@ def main():
     bwd_ms = timed(run_bwd, max(1, args.steps // 2), max(1, args.warmup // 2))
     bwd_tflops = flop_fraction * w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
 
-    traffic = load_traffic(w.name) if args.splits == 0 and not args.mask else None
+    traffic = load_traffic(w.name) if args.splits == 0 and not args.mask and hkv == w.H else None
     if args.mask:
         kernel = "fwd_kernel<%d,%s,key mask>" % (w.D, "causal" if w.causal else "full")
     elif args.splits > 0:
@@ -254,7 +262,7 @@ def main():
                            "(another machine: context only)" if w is workloads.HEADLINE else None,
         "dtype": w.dtype,
         "data": "synthetic: seeded i.i.d. N(0,1) rounded to %s (seed %d)" % (w.dtype, w.seed),
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "causal": w.causal,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": hkv, "N": w.N, "D": w.D, "causal": w.causal,
                    "scale": w.scale},
         "pct_mfma_peak": round(100 * tflops / PEAK_TFLOPS_FP16, 2),
         "roofline": {
@@ -274,6 +282,9 @@ def main():
             "flops_counted": "10*B*H*N^2*D (causal: half): five N x N x D products",
         },
     }
+    if hkv != w.H:  # a different workload from the one the page's number is for
+        rec["vs_baseline"] = None
+        rec["vs_baseline_ref"] = None
     if args.mask:
         rec["mask"] = {"kind": args.mask, "visible_pair_fraction": round(flop_fraction, 4),
                        "mask_tiles_ms": round(mask_ms, 4),
