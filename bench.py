@@ -205,7 +205,8 @@ def main():
         def run_fwd():
             fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
-    ws = torch.empty(max(256, fa.bwd_workspace_bytes(w.B, w.H, w.N, w.D, w.causal, 0 if w.dtype == "fp16" else 1)),
+    ws = torch.empty(max(256, fa.bwd_gqa_workspace_bytes(w.B, w.H, hkv, w.N, w.D, w.causal,
+                                                         0 if w.dtype == "fp16" else 1)),
                      dtype=torch.uint8, device=dev)
 
     def run_bwd():

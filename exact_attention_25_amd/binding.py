@@ -64,6 +64,8 @@ def load_library():
     lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_gqa_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    lib.fa_bwd_gqa_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_mask_tiles_bytes.argtypes = [_i64, _i64]
     lib.fa_mask_tiles_bytes.restype = ctypes.c_size_t
     lib.fa_mask_tiles.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_size_t, _vp]
@@ -118,6 +120,10 @@ def fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits):
 
 def bwd_workspace_bytes(B, H, N, D, causal, dtype):
     return int(load_library().fa_bwd_workspace_bytes(B, H, N, D, int(causal), int(dtype)))
+
+
+def bwd_gqa_workspace_bytes(B, H, H_kv, N, D, causal, dtype):
+    return int(load_library().fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, D, int(causal), int(dtype)))
 
 
 def fa_mask_tiles_bytes(B, N):
@@ -247,7 +253,7 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     code = _dtype_code(q)
-    need = bwd_workspace_bytes(B, H, N, D, causal, code)
+    need = bwd_gqa_workspace_bytes(B, H, hkv, N, D, causal, code)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -320,7 +326,7 @@ def bwd_masked(q, k, v, o, lse, dout, tiles, causal=False, scale=None, workspace
     if tiles.numel() < fa_mask_tiles_bytes(B, N):
         raise ValueError("tile table too small for B=%d N=%d" % (B, N))
     code = _dtype_code(q)
-    need = bwd_workspace_bytes(B, H, N, D, causal, code)
+    need = bwd_gqa_workspace_bytes(B, H, hkv, N, D, causal, code)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

@@ -93,9 +93,21 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
   return a;
 }
 
+// Backward workspace: Delta (FP32 [B*H*N]), then, when the dK/dV pass splits
+// grouped query heads into P > 1 parts, FP32 partial dK and dV
+// [P][B*H_kv*N][D] each; every section 256-byte aligned.
+size_t bwd_workspace_layout(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D) {
+  const size_t delta_bytes = align256(static_cast<size_t>(B * H * N) * sizeof(float));
+  const int parts = fa::bwd_head_parts(B, H, H_kv, N);
+  if (parts <= 1) return delta_bytes;
+  const size_t part_bytes = align256(static_cast<size_t>(parts) * static_cast<size_t>(B * H_kv * N) *
+                                     static_cast<size_t>(D) * sizeof(float));
+  return delta_bytes + 2 * part_bytes;
+}
+
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, float scale,
-                     void* workspace) {
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                     float scale, void* workspace) {
   fa::BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -114,6 +126,18 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   a.mask = no_mask();
+  // Grouped heads: query-head parts of the dK/dV pass and their FP32 partial
+  // sums, placed after Delta in the workspace (see bwd_workspace_layout).
+  a.head_parts = fa::bwd_head_parts(B, H, H_kv, N);
+  a.part_dk = nullptr;
+  a.part_dv = nullptr;
+  if (a.head_parts > 1) {
+    const size_t delta_bytes = align256(static_cast<size_t>(B * H * N) * sizeof(float));
+    const size_t part_bytes = align256(static_cast<size_t>(a.head_parts) * static_cast<size_t>(B * H_kv * N) *
+                                       static_cast<size_t>(D) * sizeof(float));
+    a.part_dk = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes);
+    a.part_dv = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes + part_bytes);
+  }
   return a;
 }
 
@@ -139,7 +163,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
-  const size_t need = align256(static_cast<size_t>(B * H * N) * sizeof(float));
+  const size_t need = bwd_workspace_layout(B, H, H_kv, N, D);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   return FA_OK;
@@ -249,13 +273,19 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int ca
   return align256(static_cast<size_t>(B * H * N) * sizeof(float));
 }
 
+size_t fa_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, int causal,
+                                  int dtype) {
+  if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK || check_heads(H, H_kv) != FA_OK) return 0;
+  return bwd_workspace_layout(B, H, H_kv, N, D);
+}
+
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, int causal,
                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
                            workspace_bytes);
   if (st != FA_OK) return st;
-  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, scale, workspace);
+  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, scale, workspace);
   return status_of(fa::launch_bwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -275,7 +305,7 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, co
   if (st != FA_OK) return st;
   if (!tiles) return FA_ERR_NULL;
   if (!aligned16(tiles)) return FA_ERR_ALIGN;
-  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, scale, workspace);
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, scale, workspace);
   a.mask = mask_tiles_view(tiles, B, N);
   return status_of(
       fa::launch_bwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));

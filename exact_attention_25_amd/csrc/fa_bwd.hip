@@ -155,8 +155,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   const int64_t N = a.N;
   const int G = a.H / a.Hkv;              // query heads per K/V head
   const int BHkv = a.BH / G;
+  const int n_parts = a.head_parts;
   const int bhk = blockIdx.x % BHkv;       // K/V head; its query heads are bhk*G .. bhk*G+G-1
-  const int kt = blockIdx.x / BHkv;        // key tiles heaviest (lowest) first
+  const int part = (blockIdx.x / BHkv) % n_parts;
+  const int kt = blockIdx.x / (BHkv * n_parts);  // key tiles heaviest (lowest) first
+  const int j_begin = part * G / n_parts, j_end = (part + 1) * G / n_parts;  // this part's query heads
   const int64_t head = (int64_t)bhk * N * D;
 
   const int k0w = kt * BK + wave * 32;
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   // position's tile (jn, qtn) into the other buffers.
   const int qt_end = wg_any ? n_qt : qt_begin;  // workgroup-uniform
   const int nq = qt_end - qt_begin;
-  const int n_pos = G * nq;
+  const int n_pos = (j_end - j_begin) * nq;
   auto load = [&](int j, int qt, u32x4* Qn, u32x4* Gn) {
     const int64_t off = (int64_t)(bhk * G + j) * N * D + (int64_t)qt * BQ * D;
     const int valid = min(BQ, (int)N - qt * BQ);
@@ -322,11 +325,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   };
 
   if (n_pos > 0) {
-    load(0, qt_begin, lq0, lg0);
-    fetch_rows(0, qt_begin);
+    load(j_begin, qt_begin, lq0, lg0);
+    fetch_rows(j_begin, qt_begin);
     put_rows(ll0, ld0);
   }
-  int j_c = 0, qt_c = qt_begin;
+  int j_c = j_begin, qt_c = qt_begin;
   for (int p = 0; p < n_pos; p += 2) {
     int j1 = j_c, qt1 = qt_c;
     advance(j1, qt1);
@@ -347,6 +350,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
       dk[i] = f32x16{};
       dv[i] = f32x16{};
     }
+  }
+  if (n_parts > 1) {  // FP32 partial sums of this part's query heads
+    const int64_t prow = ((int64_t)part * BHkv + bhk) * N + my_k;
+    float* pk = a.part_dk + prow * D;
+    float* pv = a.part_dv + prow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = db * 32 + rq * 8 + g * 4;
+        *(f32x4*)(pk + d) = f32x4{dk[db][rq * 4 + 0], dk[db][rq * 4 + 1], dk[db][rq * 4 + 2], dk[db][rq * 4 + 3]};
+        *(f32x4*)(pv + d) = f32x4{dv[db][rq * 4 + 0], dv[db][rq * 4 + 1], dv[db][rq * 4 + 2], dv[db][rq * 4 + 3]};
+      }
+    return;
   }
   uint16_t* dk_row = a.dk + head + (int64_t)my_k * D;
   uint16_t* dv_row = a.dv + head + (int64_t)my_k * D;
@@ -562,6 +579,29 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
                 pack2<T>(dq[db][rq * 4 + 2] * sc, dq[db][rq * 4 + 3] * sc)};
 }
 
+// Sum of the query-head parts' FP32 dK, dV (in part order, so the result is
+// reproducible), dK scaled, both rounded to T: D/4 threads per key row.
+template <int D, class T>
+__global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(const float* __restrict__ part_dk,
+                                                               const float* __restrict__ part_dv,
+                                                               uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                                                               int64_t rows, int n_parts, float scale) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = kThreads / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row >= rows) return;
+  f32x4 sk = f32x4{0.f, 0.f, 0.f, 0.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < n_parts; ++p) {
+    const int64_t off = ((int64_t)p * rows + row) * D + c * 4;
+    sk += *(const f32x4*)(part_dk + off);
+    sv += *(const f32x4*)(part_dv + off);
+  }
+  sk *= scale;
+  *(u32x2*)(dk + row * D + c * 4) = u32x2{pack2<T>(sk[0], sk[1]), pack2<T>(sk[2], sk[3])};
+  *(u32x2*)(dv + row * D + c * 4) = u32x2{pack2<T>(sv[0], sv[1]), pack2<T>(sv[2], sv[3])};
+}
+
 template <int D, bool CAUSAL, class T, bool MASK>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.N;
@@ -572,10 +612,18 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t n_ktiles = (a.N + 127) / 128;
   const int64_t n_kv_heads = a.BH / (a.H / a.Hkv);
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(n_kv_heads * n_ktiles)), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(n_kv_heads * n_ktiles * a.head_parts)),
+                     dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.head_parts > 1) {
+    const int64_t kv_rows = n_kv_heads * a.N;
+    constexpr int rpb = kThreads / (D / 4);
+    hipLaunchKernelGGL((dkdv_reduce_kernel<D, T>), dim3((unsigned)((kv_rows + rpb - 1) / rpb)), dim3(kThreads), 0,
+                       stream, a.part_dk, a.part_dv, a.dk, a.dv, kv_rows, a.head_parts, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t n_qtiles = (a.N + 127) / 128;
   hipLaunchKernelGGL((dq_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(a.BH * n_qtiles)), dim3(kThreads), 0, stream,
                      a);

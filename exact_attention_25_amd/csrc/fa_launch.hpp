@@ -63,7 +63,26 @@ struct BwdArgs {
   float scale;       // the caller's scale (for dQ, dK)
   float scale_log2;  // scale * log2(e)
   MaskTiles mask;    // key-padding mask mode only
+  // Grouped heads: the G query heads of a K/V head are split into head_parts
+  // parts; with more than one, each part writes FP32 partial dK, dV
+  // [head_parts][B*Hkv][N][D] (dK not yet scaled) and a reduce kernel sums them.
+  int head_parts;
+  float* part_dk;
+  float* part_dv;
 };
+
+// Number of query-head parts for the dK/dV pass: 1 when one workgroup per
+// (K/V head, 128 keys) already gives kWantWorkgroups, else enough parts
+// (at most G) to get there -- MQA with few K/V heads would otherwise leave
+// most of the 256 CUs idle.
+constexpr int64_t kWantWorkgroups = 1024;
+inline int bwd_head_parts(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
+  const int64_t G = H / Hkv;
+  const int64_t wgs = B * Hkv * ((N + 127) / 128);
+  if (G <= 1 || wgs >= kWantWorkgroups) return 1;
+  const int64_t parts = (kWantWorkgroups + wgs - 1) / wgs;
+  return (int)(parts < G ? parts : G);
+}
 
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);

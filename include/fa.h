@@ -167,12 +167,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_bwd_gqa_workspace_bytes -- bytes of device workspace fa_bwd_gqa and
+ * fa_bwd_masked need: Delta (4*B*H*N), plus, when the dK/dV pass splits the
+ * query heads of each group into P > 1 parts (few K/V heads: the pass would
+ * otherwise have too few workgroups to fill the GPU), FP32 partial dK and
+ * dV of 4*P*B*H_kv*N*D bytes each; sections rounded up to 256.  Returns 0
+ * for arguments fa_bwd_gqa would reject.  Equals fa_bwd_workspace_bytes
+ * when H_kv = H.
+ */
+size_t fa_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                                  int causal, int dtype);
+
+/*
  * fa_bwd_gqa -- fa_bwd for a forward computed by fa_fwd_gqa.
  *   dk, dv : [B, H_kv, N, D]; every other tensor as in fa_fwd_gqa / fa_bwd.
  * The gradient of a shared K/V head is the sum over the H / H_kv query heads
- * that read it, accumulated in FP32 registers by one workgroup per 128 keys
- * (it walks the query tiles of every head of the group), so the result is
- * still bitwise reproducible.  Workspace: fa_bwd_workspace_bytes(B, H, ...).
+ * that read it.  One workgroup per 128 keys walks the query tiles of its
+ * part of the group's heads, accumulating in FP32 registers; with several
+ * parts a reduce kernel adds the parts' FP32 sums in a fixed order, so the
+ * result is bitwise reproducible either way.
+ * Workspace: fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, D, ...).
  */
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                const float* lse, const void* dout,
@@ -239,8 +253,9 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
 /*
  * fa_bwd_masked -- fa_bwd_gqa for a forward computed by fa_fwd_masked with
  * the same tile table.  Hidden keys get dK = dV = 0 exactly; rows without a
- * visible key (LSE = -inf) get dQ = 0.  Arguments, workspace and errors as
- * for fa_bwd_gqa; FA_ERR_NULL for a NULL table.
+ * visible key (LSE = -inf) get dQ = 0.  Arguments, workspace
+ * (fa_bwd_gqa_workspace_bytes) and errors as for fa_bwd_gqa; FA_ERR_NULL for
+ * a NULL table.
  */
 int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dout,

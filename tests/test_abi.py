@@ -24,7 +24,8 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_gqa", "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_fwd",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes", "fa_bwd_masked",
+                                    "fa_bwd_workspace_bytes", "fa_fwd",
                                     "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
                                     "fa_status_str"]
@@ -177,3 +178,17 @@ def test_bwd_gqa_rejects(kw, code):
     assert fb.fa_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
                          a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"],
                          a["ws"], a["wsb"], None) == code
+
+
+def test_bwd_gqa_workspace_bytes():
+    # H_kv = H: Delta only, as fa_bwd_workspace_bytes
+    assert fb.bwd_gqa_workspace_bytes(2, 4, 4, 100, 64, 1, 0) == fb.bwd_workspace_bytes(2, 4, 100, 64, 1, 0)
+    # enough workgroups (B*H_kv*ceil(N/128) >= 1024): one part, Delta only
+    assert fb.bwd_gqa_workspace_bytes(1, 64, 8, 16384, 128, 1, 0) == 64 * 16384 * 4
+    # MQA, B1 H32 N8192: 64 workgroups -> 16 parts of FP32 dK and dV partials
+    delta = 32 * 8192 * 4
+    part = 16 * 8192 * 128 * 4
+    assert fb.bwd_gqa_workspace_bytes(1, 32, 1, 8192, 128, 1, 0) == delta + 2 * part
+    # parts never exceed the group size
+    assert fb.bwd_gqa_workspace_bytes(1, 2, 1, 64, 64, 0, 1) == 2 * 64 * 4 + 2 * 2 * 64 * 64 * 4
+    assert fb.bwd_gqa_workspace_bytes(1, 4, 3, 64, 64, 0, 0) == 0

@@ -113,3 +113,22 @@ def test_gqa_equals_mha_on_repeated_heads_bitwise():
     dq2, _, _ = fa.bwd(q, k_rep, v_rep, o2, l2, do, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(dq1, dq2)
+
+
+def test_bwd_gqa_uneven_head_parts():
+    # B*H_kv*ceil(N/128) = 256 workgroups -> the dK/dV pass splits each group
+    # of G = 6 query heads into 4 parts of 1, 2, 1, 2 heads
+    B, H, Hkv, N, D = 8, 12, 2, 2048, 64
+    assert fa.bwd_gqa_workspace_bytes(B, H, Hkv, N, D, 1, 0) == B * H * N * 4 + 2 * 4 * B * Hkv * N * D * 4
+    inp = gqa_inputs(B, H, Hkv, N, D, "fp16", 6500)
+    q, k, v, do = (to_dev(inp[n], "fp16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for b, hk in ((0, 0), (5, 1)):
+        hs = slice(hk * 6, hk * 6 + 6)
+        sl = (slice(b, b + 1),)
+        sub = [inp["q"][sl][:, hs], inp["k"][sl][:, hk:hk + 1], inp["v"][sl][:, hk:hk + 1], inp["do"][sl][:, hs]]
+        ref = attention_backward(*sub, True, 0.125)
+        got = [to_host(dq[sl][:, hs]), to_host(dk[sl][:, hk:hk + 1]), to_host(dv[sl][:, hk:hk + 1])]
+        assert_grads_close(got, ref, "b=%d group %d" % (b, hk))
