@@ -16,7 +16,8 @@ written from the definitions on these pages (cited by title and section):
   §4.2.1-4.2.2 forward tiling and recurrence, §4.3.1 backward formulas.
 * [FA-WHY]   "Why FlashAttention does not need to store the attention matrix"
   (jefxiong.cn) -- §3.1 safe softmax, §3.2 online recurrence and LSE, §3.3
-  backward with the scale factor, §4.5 causal block skipping.
+  backward with the scale factor, §4.5 causal block skipping, §05 dropout
+  regenerated from the Philox seed and offset.
 * [FA-MI50]  "FlashAttention dataflow and engineering validation on MI50"
   (mpbf.cn/news/61284) -- §2.2 worked example, §3.3 backward correction term,
   §4.3 block-level flags of padding masks, §5.1 random mask patterns.
@@ -24,9 +25,11 @@ written from the definitions on these pages (cited by title and section):
 Modules
 -------
 ``attention``  plain-definition forward / backward (materialised rows,
-               optional key-padding mask), online tiled forward, state
-               merge, key-split partial states, block-level mask flags,
-               pure-Python brute force.
+               optional key-padding mask, grouped K/V heads, dropout),
+               online tiled forward, state merge, key-split partial states,
+               block-level mask flags, pure-Python brute force.
+``dropout``    Philox4x64-10 and the dropout keep mask regenerated from
+               (seed, offset).
 
 Every function in ``attention`` is pinned by ``tests/test_oracle.py``; none is
 "parity unpinned".
@@ -43,4 +46,10 @@ from .attention import (  # noqa: F401
     brute_force_forward,
     causal_tile_count,
     key_tile_words,
+)
+from .dropout import (  # noqa: F401
+    dropout_keep,
+    dropout_threshold,
+    philox4x64,
+    philox4x64_array,
 )

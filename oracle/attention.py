@@ -39,6 +39,8 @@ import math
 
 import numpy as np
 
+from .dropout import dropout_keep, dropout_threshold
+
 NEG_INF = -np.inf
 
 
@@ -105,7 +107,18 @@ def _visibility(key_mask, B, N):
     return vis
 
 
-def attention_forward(q, k, v, causal, scale, row_block=256, rows=None, key_mask=None):
+def _drop(dropout, B, H, N, b, h, rows, nk):
+    """Keep mask times the keep scale for query rows ``rows`` of head (b, h),
+    over keys 0..nk-1, or None without dropout.  ``dropout`` = (p, seed, offset)."""
+    if dropout is None:
+        return None
+    p, seed, offset = dropout
+    _, keep_scale = dropout_threshold(p)
+    keep = dropout_keep(B, H, N, p, seed, offset, rows=rows, heads=[(b, h)])[0][:, :nk]
+    return keep * keep_scale
+
+
+def attention_forward(q, k, v, causal, scale, row_block=256, rows=None, key_mask=None, dropout=None):
     """O = softmax(scale * Q K^T + M) V and LSE, by the plain definition.
 
     For every (b, h) and every block of ``row_block`` query rows the complete
@@ -118,6 +131,8 @@ def attention_forward(q, k, v, causal, scale, row_block=256, rows=None, key_mask
     computed (for every head) and the outputs have len(rows) in place of N.
     ``key_mask``: optional [B, N] key-padding mask (see the module notes);
     rows without a visible key get O = 0 and LSE = -inf.
+    ``dropout``: optional (p, seed, offset); O = (P * Z / (1 - p')) V with the
+    keep mask Z of ``oracle.dropout`` (LSE stays that of the undropped P).
 
     Returns (O, LSE) as float64 arrays of shape [B,H,R,D] and [B,H,R].
     """
@@ -138,7 +153,8 @@ def attention_forward(q, k, v, causal, scale, row_block=256, rows=None, key_mask
                 s, nk = _scores_block(qh, kh, 0, 0, causal, scale, rows=sel[r0:r1],
                                       vis=None if vis is None else vis[b])
                 p, m, l = _safe_softmax_rows(s)
-                o[b, h, r0:r1] = p @ vh[:nk]
+                z = _drop(dropout, B, H, N, b, h, sel[r0:r1], nk)
+                o[b, h, r0:r1] = (p if z is None else p * z) @ vh[:nk]
                 lse[b, h, r0:r1] = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
     return o, lse
 
@@ -157,7 +173,7 @@ def attention_probs(q, k, causal, scale):
     return p
 
 
-def attention_backward(q, k, v, do, causal, scale, row_block=256, key_mask=None):
+def attention_backward(q, k, v, do, causal, scale, row_block=256, key_mask=None, dropout=None):
     """dQ, dK, dV of L with dL/dO = ``do``, by the plain definition.
 
     With P the forward probabilities and G = dO:
@@ -168,6 +184,9 @@ def attention_backward(q, k, v, do, causal, scale, row_block=256, key_mask=None)
     materialised in float64 a block of query rows at a time; sums over
     query rows are split over those blocks.  With ``key_mask``, P is the
     masked softmax (zero for invisible keys and for rows with no visible key).
+    With ``dropout`` (p, seed, offset) and D = Z / (1 - p') the scaled keep
+    mask, the output is O = (P*D) V, so dV = (P*D)^T G, dP = (G V^T) * D,
+    Delta_i = sum_j P_ij dP_ij (= rowsum(G * O)) and dS = P * (dP - Delta).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     _check4(q, k, v, do)
@@ -186,8 +205,11 @@ def attention_backward(q, k, v, do, causal, scale, row_block=256, key_mask=None)
                 s, nk = _scores_block(qh, kh, i0, i1, causal, scale, vis=None if vis is None else vis[b])
                 p, _, _ = _safe_softmax_rows(s)
                 g = gh[i0:i1]
-                dv[b, hk, :nk] += p.T @ g
+                z = _drop(dropout, B, H, N, b, h, np.arange(i0, i1), nk)
+                dv[b, hk, :nk] += (p if z is None else p * z).T @ g
                 dp = g @ vh[:nk].T
+                if z is not None:
+                    dp = dp * z
                 delta = (p * dp).sum(axis=1)
                 ds = p * (dp - delta[:, None])
                 dq[b, h, i0:i1] = scale * (ds @ kh[:nk])
@@ -383,13 +405,16 @@ def key_tile_words(key_mask, block=64):
 # ---------------------------------------------------------------------------
 # Pure-Python brute force for tiny inputs.
 # ---------------------------------------------------------------------------
-def brute_force_forward(q, k, v, causal, scale, visible=None):
+def brute_force_forward(q, k, v, causal, scale, visible=None, keep=None, keep_scale=1.0):
     """Attention of one head with Python floats, math.exp and math.fsum.
 
     q, k, v: nested sequences [N][D] (N <= 8 expected).  Direct transcription
     of the definition ([FA-CUDA] §1, safe softmax per [FA-WHY] §3.1), no
     numpy.  ``visible``: optional sequence of N truth values; only those keys
-    take part.  A row with no key gets O = 0 and LSE = -inf.
+    take part.  A row with no key gets O = 0 and LSE = -inf.  ``keep``:
+    optional [N][N] truth values of a dropout mask; the probability of a
+    dropped pair is zeroed and a kept one multiplied by ``keep_scale`` before
+    it weights V (the LSE is unchanged).
     Returns (O as list of lists, LSE as list).
     """
     n = len(q)
@@ -406,8 +431,10 @@ def brute_force_forward(q, k, v, causal, scale, visible=None):
         e = [math.exp(x - m) for x in s]
         tot = math.fsum(e)
         row = []
+        w = [e[idx] * ((keep_scale if keep[i][j] else 0.0) if keep is not None else 1.0)
+             for idx, j in enumerate(keys)]
         for t in range(d):
-            row.append(math.fsum(e[idx] * v[j][t] for idx, j in enumerate(keys)) / tot)
+            row.append(math.fsum(w[idx] * v[j][t] for idx, j in enumerate(keys)) / tot)
         out.append(row)
         lse.append(m + math.log(tot))
     return out, lse

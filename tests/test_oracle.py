@@ -508,3 +508,121 @@ def test_grouped_heads_finite_differences():
 def test_grouped_heads_reject_non_divisor():
     with pytest.raises(ValueError):
         attention_forward(_rand(530, 1, 3, 4, 2), _rand(531, 1, 2, 4, 2), _rand(532, 1, 2, 4, 2), False, 1.0)
+
+
+# --------------------------------------------------------------------------
+# Dropout regenerated from Philox4x64-10 (seed, offset)
+# --------------------------------------------------------------------------
+from oracle import dropout_keep, dropout_threshold, philox4x64, philox4x64_array  # noqa: E402
+
+
+def _numpy_philox_block(counter, key):
+    """numpy's own Philox4x64-10 bit generator: it raises the 256-bit counter
+    by one before each block, so start it one below the wanted counter."""
+    c = sum(int(x) << (64 * i) for i, x in enumerate(counter)) - 1
+    c %= 1 << 256
+    words = np.array([(c >> (64 * i)) & ((1 << 64) - 1) for i in range(4)], dtype=np.uint64)
+    bg = np.random.Philox(counter=words, key=np.array(key, dtype=np.uint64))
+    return [int(x) for x in bg.random_raw(4)]
+
+
+@pytest.mark.parametrize("counter,key", [
+    ([0, 0, 0, 0], [0, 0]),
+    ([1, 2, 3, 4], [5, 6]),
+    ([0, 7, 0, 0], [0xFFFFFFFFFFFFFFFF, 1]),
+    ([(1 << 64) - 1, (1 << 64) - 1, 12, 99], [0x0123456789ABCDEF, 0xFEDCBA9876543210]),
+    ([0x5555, 4095, 31, 2 ** 40], [42, 0]),
+])
+def test_philox_matches_numpy_bit_generator(counter, key):
+    assert philox4x64(counter, key) == _numpy_philox_block(counter, key)
+
+
+def test_philox_array_matches_scalar():
+    rng = np.random.default_rng(600)
+    c = rng.integers(0, 2 ** 63, size=(4, 50), dtype=np.uint64) * np.uint64(2) + np.uint64(1)
+    key = (0x9E3779B97F4A7C15, 0x123456789)
+    w = philox4x64_array(c[0], c[1], c[2], c[3], *key)
+    for n in range(50):
+        assert [int(x[n]) for x in w] == philox4x64([int(c[r, n]) for r in range(4)], key)
+
+
+def test_dropout_keep_mapping_per_element():
+    B, H, N, p, seed, offset = 2, 3, 70, 0.37, 0xABCDEF, 5
+    keep = dropout_keep(B, H, N, p, seed, offset)
+    thr, _ = dropout_threshold(p)
+    rng = np.random.default_rng(601)
+    for _ in range(200):
+        b, h, i, j = (int(rng.integers(0, x)) for x in (B, H, N, N))
+        w = philox4x64([j // 16, i, b * H + h, offset], [seed, 0])
+        value = (w[(j % 16) // 4] >> (16 * (j % 4))) & 0xFFFF
+        assert keep[b, h, i, j] == (value >= thr)
+
+
+def test_dropout_keep_rate_and_streams():
+    B, H, N, p = 1, 2, 600, 0.3
+    keep = dropout_keep(B, H, N, p, 7, 0)
+    thr, scale = dropout_threshold(p)
+    q_keep = 1 - thr / 65536
+    n = keep.size
+    assert abs(keep.mean() - q_keep) < 5 * math.sqrt(q_keep * (1 - q_keep) / n)
+    assert abs(scale - 1 / q_keep) < 1e-15 and thr == 19660
+    assert np.array_equal(keep, dropout_keep(B, H, N, p, 7, 0))          # regenerated, not stored
+    other = dropout_keep(B, H, N, p, 7, 1)                               # the next offset
+    assert 0.3 < np.mean(keep != other) < 0.5
+    assert dropout_keep(1, 1, 20, 0.0, 3, 0).all()
+
+
+def test_dropout_zero_probability_changes_nothing():
+    q, k, v = _rand(610, 1, 2, 50, 8), _rand(611, 1, 2, 50, 8), _rand(612, 1, 2, 50, 8)
+    a = attention_forward(q, k, v, True, 0.3)
+    b = attention_forward(q, k, v, True, 0.3, dropout=(0.0, 99, 3))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_brute_force_agrees(causal):
+    n, d, p, seed, offset = 7, 3, 0.4, 77, 2
+    q, k, v = _rand(620, n, d), _rand(621, n, d), _rand(622, n, d)
+    keep = dropout_keep(1, 1, n, p, seed, offset)[0, 0]
+    _, ks = dropout_threshold(p)
+    ob, lb = brute_force_forward(q.tolist(), k.tolist(), v.tolist(), causal, 0.5, keep=keep.tolist(), keep_scale=ks)
+    o, lse = attention_forward(_heads(q), _heads(k), _heads(v), causal, 0.5, dropout=(p, seed, offset))
+    assert np.abs(o[0, 0] - np.array(ob)).max() < 1e-14
+    assert np.abs(lse[0, 0] - np.array(lb)).max() < 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_backward_matches_finite_differences(causal):
+    n, d = 6, 3
+    q, k, v = _rand(630, 1, 2, n, d), _rand(631, 1, 2, n, d), _rand(632, 1, 2, n, d)
+    do = _rand(633, 1, 2, n, d)
+    drop = (0.35, 1234, 9)
+    grads = attention_backward(q, k, v, do, causal, 0.6, dropout=drop)
+
+    def loss(q_, k_, v_):
+        return float((attention_forward(q_, k_, v_, causal, 0.6, dropout=drop)[0] * do).sum())
+
+    h = 1e-6
+    for gi, name in enumerate("qkv"):
+        base = [q, k, v]
+        num = np.zeros_like(base[gi])
+        for idx in np.ndindex(base[gi].shape):
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[gi][idx] += h
+            minus[gi][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        assert np.abs(num - grads[gi]).max() < 1e-8, name
+
+
+def test_dropout_delta_equals_rowsum_do_o():
+    # the backward's correction term still equals rowsum(dO * O) with the
+    # dropped O, which is what the GPU's preprocessing pass computes
+    n, d, p, seed, offset = 30, 8, 0.25, 5, 0
+    q, k, v, do = (_rand(640 + i, 1, 1, n, d) for i in range(4))
+    o, _ = attention_forward(q, k, v, True, 0.4, dropout=(p, seed, offset))
+    prob = attention_probs(q[0, 0], k[0, 0], True, 0.4)
+    keep = dropout_keep(1, 1, n, p, seed, offset)[0, 0]
+    _, ks = dropout_threshold(p)
+    dp = (do[0, 0] @ v[0, 0].T) * keep * ks
+    assert np.abs((prob * dp).sum(axis=1) - (do[0, 0] * o[0, 0]).sum(axis=1)).max() < 1e-13
