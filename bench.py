@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--mode", default="bench", choices=["bench", "copy", "fwd-only", "bwd-only"])
     p.add_argument("--splits", type=int, default=0,
                    help="time fa_fwd_splitkv with this many key splits (split pass + merge) instead of fa_fwd")
+    p.add_argument("--dropout", type=float, default=0.0,
+                   help="time fa_fwd_dropout / fa_bwd_dropout with this dropout probability (seed 1234, offset 0)")
     p.add_argument("--kv-heads", type=int, default=0,
                    help="grouped heads: K and V get this many heads (must divide H); 0 = H")
     p.add_argument("--mask", default=None, choices=["lengths", "random", "blocks", "all"],
@@ -192,7 +194,12 @@ def main():
         torch.cuda.synchronize()
         mask_ms = (time.perf_counter() - t0) / 10 * 1e3
 
-    if args.mask:
+    if args.mask and args.dropout:
+        sys.exit("--mask and --dropout are separate entry points; pick one")
+    if args.dropout:
+        def run_fwd():
+            fa.fwd_dropout(q, k, v, args.dropout, 1234, 0, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    elif args.mask:
         def run_fwd():
             fa.fwd_masked(q, k, v, tiles, causal=w.causal, scale=w.scale, out=o, lse=lse)
     elif args.splits > 0:
@@ -210,6 +217,9 @@ def main():
                      dtype=torch.uint8, device=dev)
 
     def run_bwd():
+        if args.dropout:
+            return fa.bwd_dropout(q, k, v, o, lse, do, args.dropout, 1234, 0, causal=w.causal, scale=w.scale,
+                                  workspace=ws)
         if args.mask:
             return fa.bwd_masked(q, k, v, o, lse, do, tiles, causal=w.causal, scale=w.scale, workspace=ws)
         return fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
@@ -241,8 +251,10 @@ def main():
     bwd_ms = timed(run_bwd, max(1, args.steps // 2), max(1, args.warmup // 2))
     bwd_tflops = flop_fraction * w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
 
-    traffic = load_traffic(w.name) if args.splits == 0 and not args.mask and hkv == w.H else None
-    if args.mask:
+    traffic = load_traffic(w.name) if args.splits == 0 and not args.mask and hkv == w.H and not args.dropout else None
+    if args.dropout:
+        kernel = "fwd_kernel<%d,%s,dropout %g>" % (w.D, "causal" if w.causal else "full", args.dropout)
+    elif args.mask:
         kernel = "fwd_kernel<%d,%s,key mask>" % (w.D, "causal" if w.causal else "full")
     elif args.splits > 0:
         kernel = "fwd_kernel<%d,%s> split x%d + merge_kernel" % (w.D, "causal" if w.causal else "full", args.splits)
@@ -283,7 +295,9 @@ def main():
             "flops_counted": "10*B*H*N^2*D (causal: half): five N x N x D products",
         },
     }
-    if hkv != w.H:  # a different workload from the one the page's number is for
+    if args.dropout:
+        rec["dropout"] = {"p": args.dropout, "seed": 1234, "offset": 0}
+    if hkv != w.H or args.dropout:  # a different workload from the one the page's number is for
         rec["vs_baseline"] = None
         rec["vs_baseline_ref"] = None
     if args.mask:

@@ -76,6 +76,16 @@ def load_library():
     lib.fa_bwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, _vp, ctypes.c_size_t, _vp]
     lib.fa_bwd_masked.restype = ctypes.c_int
+    _u64 = ctypes.c_uint64
+    lib.fa_fwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_float, _u64, _u64, _vp]
+    lib.fa_fwd_dropout.restype = ctypes.c_int
+    lib.fa_bwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float, _u64, _u64,
+                                   _vp, ctypes.c_size_t, _vp]
+    lib.fa_bwd_dropout.restype = ctypes.c_int
+    lib.fa_dropout_mask.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_float, _u64, _u64, _vp]
+    lib.fa_dropout_mask.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -124,6 +134,22 @@ def bwd_workspace_bytes(B, H, N, D, causal, dtype):
 
 def bwd_gqa_workspace_bytes(B, H, H_kv, N, D, causal, dtype):
     return int(load_library().fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, D, int(causal), int(dtype)))
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, dropout_p, seed, offset, stream):
+    return load_library().fa_fwd_dropout(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale), int(dtype),
+                                         float(dropout_p), int(seed), int(offset), stream)
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, dropout_p, seed,
+                   offset, workspace, workspace_bytes, stream):
+    return load_library().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
+                                         float(scale), int(dtype), float(dropout_p), int(seed), int(offset),
+                                         workspace, workspace_bytes, stream)
+
+
+def fa_dropout_mask(keep, B, H, N, dropout_p, seed, offset, stream):
+    return load_library().fa_dropout_mask(keep, B, H, N, float(dropout_p), int(seed), int(offset), stream)
 
 
 def fa_mask_tiles_bytes(B, N):
@@ -337,3 +363,60 @@ def bwd_masked(q, k, v, o, lse, dout, tiles, causal=False, scale=None, workspace
     if st != FA_OK:
         raise FaError(st, "fa_bwd_masked")
     return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, dropout_p, seed, offset=0, causal=False, scale=None, out=None, lse=None):
+    """fa_fwd_dropout: forward with attention dropout regenerated from
+    (seed, offset).  k, v may have fewer heads (grouped).  Returns (o, lse)."""
+    import torch
+    hkv = _kv_heads(q, k)
+    B, H, N, D = q.shape
+    _check({"q": q}, q.shape, q.dtype, q.device)
+    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check({"out": out}, q.shape, q.dtype, q.device)
+    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
+    st = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, hkv, N, D,
+                        causal, scale, _dtype_code(q), dropout_p, seed, offset, _stream_handle(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_dropout")
+    return out, lse
+
+
+def bwd_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, causal=False, scale=None, workspace=None):
+    """fa_bwd_dropout: gradients of fwd_dropout with the same (p, seed, offset)."""
+    import torch
+    hkv = _kv_heads(q, k)
+    B, H, N, D = q.shape
+    _check({"q": q, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
+    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
+    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code = _dtype_code(q)
+    need = bwd_gqa_workspace_bytes(B, H, hkv, N, D, causal, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, hkv, N, D, causal, scale, code,
+                        dropout_p, seed, offset, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                        _stream_handle(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dropout")
+    return dq, dk, dv
+
+
+def dropout_mask(B, H, N, dropout_p, seed, offset=0, device="cuda"):
+    """The keep mask [B, H, N, N] (uint8, 1 = kept) of fwd_dropout / bwd_dropout."""
+    import torch
+    keep = torch.empty((B, H, N, N), dtype=torch.uint8, device=device)
+    st = fa_dropout_mask(keep.data_ptr(), B, H, N, dropout_p, seed, offset, _stream_handle(keep.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_dropout_mask")
+    return keep

@@ -63,6 +63,18 @@ fa::MaskTiles mask_tiles_view(const void* tiles, int64_t B, int64_t N) {
   return m;
 }
 
+// Dropout parameters: thr = floor(p * 65536) (p in [0, 1)), keep scale
+// 65536 / (65536 - thr).  Returns false for p outside [0, 1).
+bool dropout_args(float p, uint64_t seed, uint64_t offset, fa::DropoutArgs* d) {
+  if (!(p >= 0.f && p < 1.f)) return false;
+  const double thr = floor(static_cast<double>(p) * 65536.0);
+  d->seed = seed;
+  d->offset = offset;
+  d->thr = static_cast<uint32_t>(thr);
+  d->keep_scale = static_cast<float>(65536.0 / (65536.0 - thr));
+  return true;
+}
+
 fa::MaskTiles no_mask() {
   fa::MaskTiles m;
   m.words = nullptr;
@@ -90,6 +102,7 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
   a.part_lse = nullptr;
   a.part_o = nullptr;
   a.mask = no_mask();
+  dropout_args(0.f, 0, 0, &a.drop);
   return a;
 }
 
@@ -126,6 +139,7 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   a.mask = no_mask();
+  dropout_args(0.f, 0, 0, &a.drop);
   // Grouped heads: query-head parts of the dK/dV pass and their FP32 partial
   // sums, placed after Delta in the workspace (see bwd_workspace_layout).
   a.head_parts = fa::bwd_head_parts(B, H, H_kv, N);
@@ -309,6 +323,44 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, co
   a.mask = mask_tiles_view(tiles, B, N);
   return status_of(
       fa::launch_bwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+}
+
+// ---- dropout ---------------------------------------------------------------
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, float dropout_p,
+                   uint64_t seed, uint64_t offset, void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
+  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
+  return status_of(
+      fa::launch_fwd_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                   int causal, float scale, int dtype, float dropout_p, uint64_t seed, uint64_t offset,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
+                           workspace_bytes);
+  if (st != FA_OK) return st;
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, scale, workspace);
+  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
+  return status_of(
+      fa::launch_bwd_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int fa_dropout_mask(uint8_t* keep, int64_t B, int64_t H, int64_t N, float dropout_p, uint64_t seed, uint64_t offset,
+                    void* stream) {
+  if (!keep) return FA_ERR_NULL;
+  if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN) return FA_ERR_SHAPE;
+  if (B > kMaxWorkgroups / H || N > (int64_t(1) << 24)) return FA_ERR_SHAPE;
+  const int64_t per_head = N * ((N + 15) / 16);  // threads per head, <= 2^44
+  if (B * H > (kMaxWorkgroups * 256) / per_head) return FA_ERR_SHAPE;
+  fa::DropoutArgs d;
+  if (!dropout_args(dropout_p, seed, offset, &d)) return FA_ERR_UNSUPPORTED;
+  return status_of(fa::launch_dropout_mask(keep, B * H, N, d, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -141,12 +141,22 @@ __device__ __forceinline__ int tr_offset(int r, int col) {
 // like the others and zeroed at the end; a wave whose 32 keys are all hidden
 // skips the products, and a workgroup with no visible key skips the loop.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, class T, bool MASK>
+// DROP (attention dropout): with Z the keep mask regenerated from the Philox
+// seed and offset and s the keep scale, dV = (P*Z*s)^T dO and
+// dS = P * ((dO V^T)*Z*s - Delta).  A lane holds one key and 16 queries, but
+// a Philox block yields 16 keys of one query, so each lane computes the
+// block of (query qb0 + lane % 32, keys k0w + 16*(lane / 32) ..) and the keep
+// bits are transposed through 128 bytes of LDS per wave.
+template <int D, bool CAUSAL, class T, bool MASK, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs a) {
+  static_assert(!(MASK && DROP), "dropout runs without a mask");
   constexpr int BK = 128, BQ = kTileRows;
   constexpr int RC = D / 8, TC = BQ * RC;
   __shared__ u32x4 lq0[TC], lq1[TC], lg0[TC], lg1[TC];
   __shared__ __attribute__((aligned(16))) float ll0[BQ], ll1[BQ], ld0[BQ], ld1[BQ];
+  // Dropout: per wave, 32 words (one per query of the block); bits 0-15
+  // keys k0w..k0w+15, bits 16-31 keys k0w+16..k0w+31.
+  __shared__ __attribute__((aligned(16))) uint32_t drop_w[DROP ? kThreads / 64 : 1][32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     }
   };
 
-  auto compute = [&](int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
+  auto compute = [&](int j, int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
     const char* Qb = (const char*)Ql;
     const char* Gb = (const char*)Gl;
     const int q0 = qt * BQ;
@@ -267,12 +277,36 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
           }
         }
       const bool diag = CAUSAL && qb0 < k0w + 31;
+      if constexpr (DROP) {
+        // this lane's Philox block: query qb0 + l32, keys k0w + 16g .. +15
+        const uint32_t row_bits = dropout_bits16(k0w / 16 + g, qb0 + l32, (uint64_t)(bhk * G + j), a.drop.seed,
+                                                 a.drop.offset, a.drop.thr);
+        asm volatile("" ::: "memory");
+        ((uint16_t*)&drop_w[wave][l32])[g] = (uint16_t)row_bits;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS ops run in order
+        // register r holds query qb0 + acc_row(r, g): words 8g .. 8g+7, 16+8g .. 16+8g+7
+        const u32x4* wv = (const u32x4*)&drop_w[wave][0];
+        const u32x4 w0 = wv[2 * g], w1 = wv[2 * g + 1], w2 = wv[4 + 2 * g], w3 = wv[5 + 2 * g];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next block rewrites it
+        const uint32_t wq[16] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
+                                 w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
+        const float ks = a.drop.keep_scale;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[r], c2, -lse_r[r]));
-        if (diag && my_k > qb0 + acc_row(r, g)) p = 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - dl_r[r]);
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], c2, -lse_r[r]));
+          if (diag && my_k > qb0 + acc_row(r, g)) p = 0.f;
+          const bool keep = (wq[r] >> l32) & 1u;
+          s[r] = keep ? p * ks : 0.f;                     // dropped, scaled P for dV
+          dp[r] = p * ((keep ? dp[r] * ks : 0.f) - dl_r[r]);  // dS
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], c2, -lse_r[r]));
+          if (diag && my_k > qb0 + acc_row(r, g)) p = 0.f;
+          s[r] = p;
+          dp[r] = p * (dp[r] - dl_r[r]);
+        }
       }
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
@@ -305,7 +339,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     copy_tile<D>(a.q + off, src0, Qn, wave, valid);
     copy_tile<D>(a.dout + off, src0, Gn, wave, valid);
   };
-  auto step = [&](int p, int qt, int jn, int qtn, const u32x4* Ql, const u32x4* Gl, const float* ll,
+  auto step = [&](int p, int j, int qt, int jn, int qtn, const u32x4* Ql, const u32x4* Gl, const float* ll,
                   const float* ld, u32x4* Qn, u32x4* Gn, float* lln, float* ldn) {
     wait_vmem();      // this wave's copies of position p have landed
     __syncthreads();  // everyone's have (and the LSE/Delta rows); position p-1 is done
@@ -313,7 +347,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
       fetch_rows(jn, qtn);  // first, so that storing them later need not wait for the tile copies
       load(jn, qtn, Qn, Gn);
     }
-    if (active) compute(qt, Ql, Gl, ll, ld);
+    if (active) compute(j, qt, Ql, Gl, ll, ld);
     if (p + 1 < n_pos) put_rows(lln, ldn);
   };
   // (j, qt) -> the next position
@@ -333,11 +367,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   for (int p = 0; p < n_pos; p += 2) {
     int j1 = j_c, qt1 = qt_c;
     advance(j1, qt1);
-    step(p, qt_c, j1, qt1, lq0, lg0, ll0, ld0, lq1, lg1, ll1, ld1);
+    step(p, j_c, qt_c, j1, qt1, lq0, lg0, ll0, ld0, lq1, lg1, ll1, ld1);
     if (p + 1 < n_pos) {
       int j2 = j1, qt2 = qt1;
       advance(j2, qt2);
-      step(p + 1, qt1, j2, qt2, lq1, lg1, ll1, ld1, lq0, lg0, ll0, ld0);
+      step(p + 1, j1, qt1, j2, qt2, lq1, lg1, ll1, ld1, lq0, lg0, ll0, ld0);
       j_c = j2;
       qt_c = qt2;
     }
@@ -392,8 +426,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
 // MASK (key-padding mask): only the non-empty key tiles of the batch
 // element's list are visited, and hidden keys of partial tiles get P = 0.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, class T, bool MASK>
+// DROP: dS^T = P^T * ((V dO^T)*Z*s - Delta), with the keep bits of the
+// S^T layout (one query per lane) as in the forward pass.
+template <int D, bool CAUSAL, class T, bool MASK, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
+  static_assert(!(MASK && DROP), "dropout runs without a mask");
   constexpr int BM = 128, BN = kTileRows;
   constexpr int RC = D / 8, TC = BN * RC;
   __shared__ u32x4 lk0[TC], lk1[TC], lv0[TC], lv1[TC];
@@ -491,10 +528,22 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
           if ((CAUSAL && key > my_q) || hidden) s[kb][r] = 0.f;
         }
     }
+    if constexpr (DROP) {
+      const float ks = a.drop.keep_scale;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t keep = dropout_bits_st(k0 + kb * 32, my_q, (uint64_t)bh, a.drop.seed, a.drop.offset,
+                                              a.drop.thr, g);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[kb][r] = s[kb][r] * (dp[kb][r] - dl);
+        for (int r = 0; r < 16; ++r)
+          dp[kb][r] = s[kb][r] * ((((keep >> r) & 1u) ? dp[kb][r] * ks : 0.f) - dl);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[kb][r] = s[kb][r] * (dp[kb][r] - dl);
+    }
     // dQ^T += K^T dS^T, 16 keys per step (registers 8*(t%2).. of block t/2).
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
@@ -602,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(const float* __re
   *(u32x2*)(dv + row * D + c * 4) = u32x2{pack2<T>(sv[0], sv[1]), pack2<T>(sv[2], sv[3])};
 }
 
-template <int D, bool CAUSAL, class T, bool MASK>
+template <int D, bool CAUSAL, class T, bool MASK, bool DROP>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.N;
   constexpr int rpb = kThreads / (D / 8);
@@ -612,7 +661,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t n_ktiles = (a.N + 127) / 128;
   const int64_t n_kv_heads = a.BH / (a.H / a.Hkv);
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(n_kv_heads * n_ktiles * a.head_parts)),
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, T, MASK, DROP>), dim3((unsigned)(n_kv_heads * n_ktiles * a.head_parts)),
                      dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -625,8 +674,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int64_t n_qtiles = (a.N + 127) / 128;
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, T, MASK>), dim3((unsigned)(a.BH * n_qtiles)), dim3(kThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, T, MASK, DROP>), dim3((unsigned)(a.BH * n_qtiles)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -634,7 +683,22 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_BWD_CASE(DD, CC, TT) \
-  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, false>(a, stream);
+  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, false, false>(a, stream);
+  FA_BWD_CASE(64, false, Fp16)
+  FA_BWD_CASE(64, true, Fp16)
+  FA_BWD_CASE(128, false, Fp16)
+  FA_BWD_CASE(128, true, Fp16)
+  FA_BWD_CASE(64, false, Bf16)
+  FA_BWD_CASE(64, true, Bf16)
+  FA_BWD_CASE(128, false, Bf16)
+  FA_BWD_CASE(128, true, Bf16)
+#undef FA_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dropout(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_BWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, false, true>(a, stream);
   FA_BWD_CASE(64, false, Fp16)
   FA_BWD_CASE(64, true, Fp16)
   FA_BWD_CASE(128, false, Fp16)
@@ -649,7 +713,7 @@ hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream
 
 hipError_t launch_bwd_masked(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_BWD_CASE(DD, CC, TT) \
-  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, true>(a, stream);
+  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, true, false>(a, stream);
   FA_BWD_CASE(64, false, Fp16)
   FA_BWD_CASE(64, true, Fp16)
   FA_BWD_CASE(128, false, Fp16)

@@ -218,6 +218,93 @@ __device__ __forceinline__ bool key_hidden(uint32_t wlo, uint32_t whi, int kb, i
   return ((wk >> (16 * (r >> 3) + (r & 7))) & 1u) == 0;
 }
 
+// ---------------------------------------------------------------------------
+// Dropout: Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011).  Per round the two 64 x 64 -> 128
+// bit products M0*c0 and M1*c2 are formed and c = (hi1 ^ c1 ^ k0, lo1,
+// hi0 ^ c3 ^ k1, lo0); the key is then bumped by the Weyl constants.
+// Query i, key j of head bh uses counter (j / 16, i, bh, offset) and key
+// (seed, 0); the 256 output bits are 16 values of 16 bits, key 16t + e
+// taking bits 16*(e % 4) .. +15 of word e / 4, and the key is kept iff its
+// value >= thr = floor(p * 65536).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+__device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                              uint64_t k1, uint64_t (&out)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kPhiloxM0, c0), lo0 = kPhiloxM0 * c0;
+    const uint64_t hi1 = __umul64hi(kPhiloxM1, c2), lo1 = kPhiloxM1 * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// 16-bit value e (0..7) of a group of 8 held in two 64-bit words.
+__device__ __forceinline__ uint32_t half8_value(uint64_t w0, uint64_t w1, int e) {
+  return (uint32_t)(((e < 4 ? w0 : w1) >> (16 * (e & 3))) & 0xFFFFu);
+}
+
+// The value of x held by the lane 32 positions away (lane-half g = lane / 32).
+__device__ __forceinline__ uint32_t xhalf_partner(uint32_t x, int g) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return g ? r[0] : r[1];
+}
+
+// Keep bits of the 16 keys a lane of an S^T accumulator holds for one
+// 32-key block (query per lane, register r holding key acc_row(r, g)):
+// the block's keys are Philox groups t0 = key0/16 and t0+1; lane-half g
+// computes group t0+g, keeps the 8 values of its own half and swaps the
+// other 8 with its partner, which needs them.  Bit r of the result is the
+// keep decision of register r.
+__device__ __forceinline__ uint32_t dropout_bits_st(int key0, int query, uint64_t bh, uint64_t seed,
+                                                    uint64_t offset, uint32_t thr, int g) {
+  uint64_t w[4];
+  philox4x64_10((uint64_t)(key0 / 16 + g), (uint64_t)(uint32_t)query, bh, offset, seed, 0, w);
+  // own half g: words 2g, 2g+1; the partner needs half 1-g of this group.
+  const uint64_t own0 = g ? w[2] : w[0], own1 = g ? w[3] : w[1];
+  const uint64_t snd0 = g ? w[0] : w[2], snd1 = g ? w[1] : w[3];
+  const uint64_t rcv0 = ((uint64_t)xhalf_partner((uint32_t)(snd0 >> 32), g) << 32) |
+                        xhalf_partner((uint32_t)snd0, g);
+  const uint64_t rcv1 = ((uint64_t)xhalf_partner((uint32_t)(snd1 >> 32), g) << 32) |
+                        xhalf_partner((uint32_t)snd1, g);
+  // registers 0-7: group t0, values 8g .. 8g+7; registers 8-15: group t0+1, same values
+  const uint64_t a0 = g ? rcv0 : own0, a1 = g ? rcv1 : own1;  // group t0, half g
+  const uint64_t b0 = g ? own0 : rcv0, b1 = g ? own1 : rcv1;  // group t0+1, half g
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bits |= (half8_value(a0, a1, e) >= thr ? 1u : 0u) << e;
+    bits |= (half8_value(b0, b1, e) >= thr ? 1u : 0u) << (8 + e);
+  }
+  return bits;
+}
+
+// Keep bits of 16 consecutive keys 16t .. 16t+15 for one query (bit e = key
+// 16t + e).
+__device__ __forceinline__ uint32_t dropout_bits16(int t, int query, uint64_t bh, uint64_t seed, uint64_t offset,
+                                                   uint32_t thr) {
+  uint64_t w[4];
+  philox4x64_10((uint64_t)t, (uint64_t)(uint32_t)query, bh, offset, seed, 0, w);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    bits |= ((uint32_t)((w[e >> 2] >> (16 * (e & 3))) & 0xFFFFu) >= thr ? 1u : 0u) << e;
+  return bits;
+}
+
 // Wait until this wave's outstanding global loads (including LDS-bound ones)
 // have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -72,9 +72,14 @@ struct FwdShape {
 // workgroup visits only the listed non-empty tiles, tests elements only in
 // tiles whose visibility word is not all ones, and a row left with no
 // visible key gets O = 0 and LSE = -inf.
-template <int D, int QB, bool CAUSAL, class T, bool SPLIT, bool MASK>
+// DROP: attention dropout ([FA-WHY]-style regeneration from a Philox seed
+// and offset, see dropout_bits_st): dropped probabilities are zeroed before
+// P weights V, the row sum l keeps the undropped ones (LSE is that of the
+// undropped softmax), and O is multiplied by the keep scale at the end.
+template <int D, int QB, bool CAUSAL, class T, bool SPLIT, bool MASK, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdArgs a) {
   static_assert(!(SPLIT && MASK), "split-K/V takes no mask");
+  static_assert(!(DROP && (SPLIT || MASK)), "dropout runs without split or mask");
   constexpr int BM = FwdShape<QB>::BM, BN = kFwdBN, NT = kFwdThreads;
   constexpr int RC = D / 8;              // 16-byte chunks per row
   constexpr int TC = BN * RC;            // chunks per K or V tile
@@ -288,6 +293,27 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(__builtin_fmaf(s[qb][kb][r], c2, -m_use[qb]));
+      if constexpr (DROP) {
+        // l sums the undropped FP32 probabilities; then the dropped ones are
+        // zeroed before packing (the keep scale is applied to O at the end).
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) lsum += s[qb][kb][r];
+        l_run[qb] += lsum;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t keep = dropout_bits_st(k0 + kb * 32, q0w + 32 * qb + ql, (uint64_t)bh, a.drop.seed,
+                                                a.drop.offset, a.drop.thr, g);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((keep >> r) & 1u)) s[qb][kb][r] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < BN / 16; ++t) pf[qb][t] = pack8<T>(s[qb][t >> 1], (t & 1) * 8);
+        continue;
+      }
       float lsum = 0.f;
 #pragma unroll
       for (int t = 0; t < BN / 16; ++t) {
@@ -411,7 +437,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     const float l_tot = xhalf_sum(l_run[qb]);
     // l_tot = 0 only for a row with no visible key (mask mode): O = 0, and
     // the LSE below evaluates to -inf + -inf = -inf.
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (DROP ? a.drop.keep_scale : 1.f);
     if (my_q >= N) continue;  // lanes past the last query
     uint16_t* Orow = a.o + head + (int64_t)my_q * D;
 #pragma unroll
@@ -465,8 +491,8 @@ hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, false, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -475,9 +501,34 @@ hipError_t launch_fwd_masked_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, true, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+                     stream, a);
   return hipGetLastError();
+}
+
+template <int D, int QB, bool CAUSAL, class T>
+hipError_t launch_fwd_dropout_t(FwdArgs a, hipStream_t stream) {
+  constexpr int BM = FwdShape<QB>::BM;
+  a.n_qtiles = (int)((a.N + BM - 1) / BM);
+  const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, false, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+// keep[bh][i][j] of the dropout mask: one thread per (bh, query, 16 keys).
+__global__ __launch_bounds__(256) void dropout_mask_kernel(uint8_t* __restrict__ keep, int64_t BH, int64_t N,
+                                                           DropoutArgs d) {
+  const int64_t T = (N + 15) / 16;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= BH * N * T) return;
+  const int64_t t = idx % T, i = (idx / T) % N, bh = idx / (T * N);
+  const uint32_t bits = dropout_bits16((int)t, (int)i, (uint64_t)bh, d.seed, d.offset, d.thr);
+  uint8_t* row = keep + (bh * N + i) * N;
+  for (int e = 0; e < 16; ++e) {
+    const int64_t j = t * 16 + e;
+    if (j < N) row[j] = (uint8_t)((bits >> e) & 1u);
+  }
 }
 
 template <int D, int QB, bool CAUSAL, class T>
@@ -485,8 +536,8 @@ hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles * a.n_splits;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true, false, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.BH * a.N;
@@ -526,6 +577,28 @@ hipError_t launch_fwd_masked(const FwdArgs& a, int D, bool causal, int dtype, hi
   FA_FWD_CASE(128, true, Bf16)
 #undef FA_FWD_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_FWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_dropout_t<DD, kFwdQB, CC, TT>(a, stream);
+  FA_FWD_CASE(64, false, Fp16)
+  FA_FWD_CASE(64, true, Fp16)
+  FA_FWD_CASE(128, false, Fp16)
+  FA_FWD_CASE(128, true, Fp16)
+  FA_FWD_CASE(64, false, Bf16)
+  FA_FWD_CASE(64, true, Bf16)
+  FA_FWD_CASE(128, false, Bf16)
+  FA_FWD_CASE(128, true, Bf16)
+#undef FA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dropout_mask(uint8_t* keep, int64_t BH, int64_t N, const DropoutArgs& d, hipStream_t stream) {
+  const int64_t threads = BH * N * ((N + 15) / 16);
+  hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, keep, BH, N,
+                     d);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {

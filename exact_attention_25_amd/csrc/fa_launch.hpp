@@ -27,6 +27,15 @@ __host__ __device__ inline int head_of_slot(int s, int BH, int G) {
   return (s % NG) * G + s / NG;
 }
 
+// Dropout (dropout mode only): Philox4x64-10 key (seed, 0), counter offset,
+// threshold floor(p * 65536) and keep scale 65536 / (65536 - thr).
+struct DropoutArgs {
+  uint64_t seed;
+  uint64_t offset;
+  uint32_t thr;
+  float keep_scale;
+};
+
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -44,6 +53,7 @@ struct FwdArgs {
   float* part_lse;
   float* part_o;
   MaskTiles mask;  // key-padding mask mode only
+  DropoutArgs drop;
 };
 
 struct BwdArgs {
@@ -63,6 +73,7 @@ struct BwdArgs {
   float scale;       // the caller's scale (for dQ, dK)
   float scale_log2;  // scale * log2(e)
   MaskTiles mask;    // key-padding mask mode only
+  DropoutArgs drop;  // dropout mode only
   // Grouped heads: the G query heads of a K/V head are split into head_parts
   // parts; with more than one, each part writes FP32 partial dK, dV
   // [head_parts][B*Hkv][N][D] (dK not yet scaled) and a reduce kernel sums them.
@@ -89,6 +100,10 @@ hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, h
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_fwd_masked(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_bwd_masked(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_fwd_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_bwd_dropout(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+// keep[b][h][i][j] (bytes, 1 = kept) of the dropout mask, for tests.
+hipError_t launch_dropout_mask(uint8_t* keep, int64_t BH, int64_t N, const DropoutArgs& d, hipStream_t stream);
 // Builds the MaskTiles sections (words, prefix, list) from a [B, N] byte mask.
 hipError_t launch_mask_tiles(const uint8_t* key_mask, int64_t B, int64_t N, uint64_t* words, int* prefix, int* list,
                              hipStream_t stream);

@@ -264,6 +264,49 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
                   int causal, float scale, int dtype, const void* tiles,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Attention dropout, regenerated instead of stored ("Why FlashAttention does
+ * not need to store the attention matrix", §05: the kernel keeps only the
+ * Philox seed and offset, and the backward pass rebuilds the same mask;
+ * "CUDA FlashAttention ...", §7: the random offset must be reproducible).
+ *
+ * Generator: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011), key
+ * (seed, 0).  For batch element b, query head h, query i and key j the
+ * counter is (j / 16, i, b*H + h, offset); the 256 output bits are 16
+ * values of 16 bits, key j = 16t + e taking bits 16*(e % 4) .. +15 of word
+ * e / 4.  Key j is kept for query i iff its value >= thr = floor(p * 65536);
+ * kept probabilities are scaled by 65536 / (65536 - thr).  So:
+ *   O = (P * Z * s) V, LSE is that of the undropped P, and the backward uses
+ *   dV = (P*Z*s)^T dO, dS = P * ((dO V^T)*Z*s - Delta), Delta = rowsum(dO*O).
+ * dropout_p must lie in [0, 1) (else FA_ERR_UNSUPPORTED); p = 0 keeps all.
+ */
+
+/* fa_fwd_dropout -- fa_fwd_gqa with dropout (p, seed, offset). */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                   int causal, float scale, int dtype,
+                   float dropout_p, uint64_t seed, uint64_t offset, void* stream);
+
+/* fa_bwd_dropout -- fa_bwd_gqa for a forward computed by fa_fwd_dropout with
+ * the same (p, seed, offset); workspace: fa_bwd_gqa_workspace_bytes. */
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv,
+                   int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                   int causal, float scale, int dtype,
+                   float dropout_p, uint64_t seed, uint64_t offset,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_dropout_mask -- write the keep mask the two calls above use:
+ * keep[b][h][i][j] = 1 (kept) or 0 (dropped), bytes, [B, H, N, N] on the
+ * device (caller-owned, any alignment).  Meant for tests and inspection: it
+ * is N*N bytes per head.  Errors: FA_ERR_NULL, FA_ERR_SHAPE (N > 2^24 or too
+ * many threads), FA_ERR_UNSUPPORTED (p outside [0, 1)), FA_ERR_HIP.
+ */
+int fa_dropout_mask(uint8_t* keep, int64_t B, int64_t H, int64_t N,
+                    float dropout_p, uint64_t seed, uint64_t offset, void* stream);
+
 /* fa_status_str -- a static, human-readable name for a status code. */
 const char* fa_status_str(int status);
 

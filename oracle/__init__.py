@@ -49,6 +49,7 @@ from .attention import (  # noqa: F401
 )
 from .dropout import (  # noqa: F401
     dropout_keep,
+    dropout_keep_rows,
     dropout_threshold,
     philox4x64,
     philox4x64_array,

@@ -39,7 +39,7 @@ import math
 
 import numpy as np
 
-from .dropout import dropout_keep, dropout_threshold
+from .dropout import dropout_keep_rows, dropout_threshold
 
 NEG_INF = -np.inf
 
@@ -109,13 +109,16 @@ def _visibility(key_mask, B, N):
 
 def _drop(dropout, B, H, N, b, h, rows, nk):
     """Keep mask times the keep scale for query rows ``rows`` of head (b, h),
-    over keys 0..nk-1, or None without dropout.  ``dropout`` = (p, seed, offset)."""
+    over keys 0..nk-1, or None without dropout.  ``dropout`` is (p, seed,
+    offset), or (p, seed, offset, head_numbers) where head_numbers[b][h] is
+    the head number the generator's counter uses (default b*H + h) -- so a
+    few heads of a larger problem can be checked on their own."""
     if dropout is None:
         return None
-    p, seed, offset = dropout
+    p, seed, offset = dropout[:3]
+    bh = int(dropout[3][b][h]) if len(dropout) > 3 else b * H + h
     _, keep_scale = dropout_threshold(p)
-    keep = dropout_keep(B, H, N, p, seed, offset, rows=rows, heads=[(b, h)])[0][:, :nk]
-    return keep * keep_scale
+    return dropout_keep_rows(bh, N, p, seed, offset, rows=rows)[:, :nk] * keep_scale
 
 
 def attention_forward(q, k, v, causal, scale, row_block=256, rows=None, key_mask=None, dropout=None):

@@ -92,24 +92,25 @@ def dropout_threshold(p):
     return thr, 65536.0 / (65536 - thr)
 
 
-def dropout_keep(B, H, N, p, seed, offset, rows=None, heads=None):
-    """Boolean keep mask [B, H, R, N] for queries ``rows`` (default all N)
-    of the heads ``heads`` (list of (b, h); default all), by the mapping in
-    the module docstring.  True = kept."""
+def dropout_keep_rows(bh, N, p, seed, offset, rows=None):
+    """Boolean keep mask [R, N] of head number bh (= b*H + h) for query rows
+    ``rows`` (default all N), by the mapping in the module docstring."""
     thr, _ = dropout_threshold(p)
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
-    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     T = -(-N // 16)
-    out = np.empty((len(heads), rows.size, T * 16), dtype=bool)
     t = np.arange(T, dtype=np.uint64)[None, :]
     i = rows.astype(np.uint64)[:, None]
-    for n, (b, h) in enumerate(heads):
-        w = philox4x64_array(t, i, np.uint64(b * H + h), np.uint64(offset), seed, 0)
-        vals = np.empty((rows.size, T, 16), dtype=np.uint64)
-        for e in range(16):
-            vals[:, :, e] = (w[e // 4] >> np.uint64(16 * (e % 4))) & np.uint64(0xFFFF)
-        out[n] = (vals >= np.uint64(thr)).reshape(rows.size, T * 16)
-    out = out[:, :, :N]
-    if heads is None or len(heads) == B * H:
-        return out.reshape(B, H, rows.size, N)
-    return out
+    w = philox4x64_array(t, i, np.uint64(bh), np.uint64(offset), seed, 0)
+    vals = np.empty((rows.size, T, 16), dtype=np.uint64)
+    for e in range(16):
+        vals[:, :, e] = (w[e // 4] >> np.uint64(16 * (e % 4))) & np.uint64(0xFFFF)
+    return (vals >= np.uint64(thr)).reshape(rows.size, T * 16)[:, :N]
+
+
+def dropout_keep(B, H, N, p, seed, offset, rows=None, heads=None):
+    """Boolean keep mask [B, H, R, N] for queries ``rows`` (default all N),
+    or [len(heads), R, N] for the (b, h) pairs in ``heads``.  True = kept."""
+    if heads is None:
+        return np.stack([dropout_keep_rows(b * H + h, N, p, seed, offset, rows)
+                         for b in range(B) for h in range(H)]).reshape(B, H, -1, N)
+    return np.stack([dropout_keep_rows(b * H + h, N, p, seed, offset, rows) for b, h in heads])

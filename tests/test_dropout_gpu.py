@@ -1,0 +1,116 @@
+"""Attention dropout on the GPU: the keep mask regenerated from (seed,
+offset) by fa_dropout_mask (bit-exact against the oracle's Philox4x64-10
+mapping), and fa_fwd_dropout / fa_bwd_dropout (through the C ABI) against
+the float64 oracle with the same (p, seed, offset).  "Why FlashAttention does
+not need to store the attention matrix" §05: only the seed and offset are
+kept; the backward pass regenerates the mask."""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_25_amd as fa
+from exact_attention_25_amd.inputs import make_inputs, round_to
+from oracle import attention_backward, attention_forward, dropout_keep
+from parity import assert_fwd_close, assert_grads_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,H,N,p,seed,offset", [
+    (1, 1, 1, 0.5, 1, 0), (2, 3, 100, 0.1, 12345, 7), (1, 2, 1000, 0.5, (1 << 64) - 1, 3),
+    (1, 1, 257, 0.9, 0xDEADBEEFCAFEF00D, (1 << 63) + 5), (1, 1, 64, 0.0, 9, 9),
+])
+def test_dropout_mask_bit_exact(B, H, N, p, seed, offset):
+    say("dropout mask B=%d H=%d N=%d p=%g" % (B, H, N, p))
+    keep = fa.dropout_mask(B, H, N, p, seed, offset)
+    torch.cuda.synchronize()
+    ref = dropout_keep(B, H, N, p, seed, offset)
+    assert np.array_equal(keep.cpu().numpy().astype(bool), ref)
+
+
+def _inputs(B, H, Hkv, N, D, dtype, seed):
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, heads in (("q", H), ("k", Hkv), ("v", Hkv), ("do", H)):
+        out[name] = round_to(rng.standard_normal((B, heads, N, D), dtype=np.float32), dtype)
+    return out
+
+
+CASES = [(1, 2, 2, 128, 64), (2, 3, 3, 200, 128), (1, 4, 2, 257, 64), (1, 1, 1, 64, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Hkv,N,D", CASES)
+def test_fwd_dropout(B, H, Hkv, N, D, causal, dtype):
+    say("fwd dropout B=%d H=%d Hkv=%d N=%d D=%d causal=%d %s" % (B, H, Hkv, N, D, causal, dtype))
+    inp = _inputs(B, H, Hkv, N, D, dtype, 7000 + N + D)
+    q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
+    drop = (0.2, 424242 + N, 11)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = fa.fwd_dropout(q, k, v, *drop, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], causal, scale, dropout=drop)
+    assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, dtype, "N=%d p=0.2" % N)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Hkv,N,D", CASES)
+def test_bwd_dropout(B, H, Hkv, N, D, causal, dtype):
+    say("bwd dropout B=%d H=%d Hkv=%d N=%d D=%d causal=%d %s" % (B, H, Hkv, N, D, causal, dtype))
+    inp = _inputs(B, H, Hkv, N, D, dtype, 7100 + N + D)
+    q, k, v, do = (to_dev(inp[n], dtype) for n in ("q", "k", "v", "do"))
+    drop = (0.3, 99 + N, 5)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = fa.fwd_dropout(q, k, v, *drop, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd_dropout(q, k, v, o, lse, do, *drop, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale, dropout=drop)
+    assert_grads_close([to_host(t) for t in (dq, dk, dv)], ref, "N=%d p=0.3" % N)
+
+
+def test_dropout_is_regenerated_deterministically():
+    inp = make_inputs(1, 4, 512, 64, "fp16", seed=7200)
+    q, k, v = (to_dev(inp[n], "fp16") for n in ("q", "k", "v"))
+    a = fa.fwd_dropout(q, k, v, 0.1, 77, 0, causal=True)
+    b = fa.fwd_dropout(q, k, v, 0.1, 77, 0, causal=True)
+    c = fa.fwd_dropout(q, k, v, 0.1, 77, 1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert not torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])  # LSE is the undropped one
+
+
+def test_dropout_zero_probability_matches_plain_forward():
+    inp = make_inputs(2, 2, 300, 128, "bf16", seed=7300, with_dout=True)
+    q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    o0, l0 = fa.fwd(q, k, v, causal=True)
+    o1, l1 = fa.fwd_dropout(q, k, v, 0.0, 1, 2, causal=True)
+    g0 = fa.bwd(q, k, v, o0, l0, do, causal=True)
+    g1 = fa.bwd_dropout(q, k, v, o1, l1, do, 0.0, 1, 2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.allclose(l0, l1, atol=1e-6, rtol=0)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
+
+
+def test_dropout_long_sampled_heads():
+    # the C5 geometry (causal fp16, H = 32, N = 4096, D = 64) with p = 0.1;
+    # a sampled head is checked alone with the counter's head number of the
+    # full problem (the oracle's head_numbers)
+    B, H, N, D = 1, 32, 4096, 64
+    inp = make_inputs(B, H, N, D, "fp16", seed=5, with_dout=True)
+    q, k, v, do = (to_dev(inp[n], "fp16") for n in ("q", "k", "v", "do"))
+    p, seed, offset = 0.1, 2024, 0
+    o, lse = fa.fwd_dropout(q, k, v, p, seed, offset, causal=True)
+    dq, dk, dv = fa.bwd_dropout(q, k, v, o, lse, do, p, seed, offset, causal=True)
+    torch.cuda.synchronize()
+    for h in (0, 17):
+        sl = (slice(0, 1), slice(h, h + 1))
+        sub = [inp[n][sl] for n in ("q", "k", "v", "do")]
+        drop = (p, seed, offset, [[h]])
+        o_ref, lse_ref = attention_forward(*sub[:3], True, 0.125, dropout=drop)
+        assert_fwd_close(to_host(o[sl]), to_host(lse[sl]), o_ref, lse_ref, "fp16", "head %d" % h)
+        grads = attention_backward(*sub, True, 0.125, dropout=drop)
+        assert_grads_close([to_host(t[sl]) for t in (dq, dk, dv)], grads, "head %d" % h)

@@ -626,3 +626,11 @@ def test_dropout_delta_equals_rowsum_do_o():
     _, ks = dropout_threshold(p)
     dp = (do[0, 0] @ v[0, 0].T) * keep * ks
     assert np.abs((prob * dp).sum(axis=1) - (do[0, 0] * o[0, 0]).sum(axis=1)).max() < 1e-13
+
+
+def test_dropout_head_numbers_select_a_head_of_a_larger_problem():
+    B, H, n, d, drop = 2, 3, 20, 4, (0.3, 8, 2)
+    q, k, v = _rand(650, B, H, n, d), _rand(651, B, H, n, d), _rand(652, B, H, n, d)
+    o, lse = attention_forward(q, k, v, False, 0.5, dropout=drop)
+    o1, _ = attention_forward(q[1:2, 2:3], k[1:2, 2:3], v[1:2, 2:3], False, 0.5, dropout=drop + ([[1 * H + 2]],))
+    assert np.array_equal(o[1:2, 2:3], o1)
