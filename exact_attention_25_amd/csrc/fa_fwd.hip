@@ -165,14 +165,22 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   // perm23 order so that register r of lane-half g holds key acc_row(r, g).
   // Each K fragment feeds the QB query blocks.
   const int krow = perm23(ql);
+  // The swizzles XOR only chunk bits below the row, so the byte offset of K
+  // row kb*32 + krow, chunk 2c + g is k_off ^ (32c), plus kb*32 rows as an
+  // immediate.  The XORs are redone on every call (the empty asm makes the
+  // base look new each time) so that only one base register stays live
+  // instead of one address register per fragment and buffer.
+  const uint32_t k_off = swz(krow * RC + g) * 16;
   auto scores = [&](const u32x4* __restrict__ Kl, f32x16 (&s)[QB][2]) {
+    uint32_t kbase = k_off;
+    asm volatile("" : "+v"(kbase));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const u32x4 kf = Kl[swz((kb * 32 + krow) * RC + c * 2 + g)];
+        const u32x4 kf = *(const u32x4*)((const char*)Kl + (kbase ^ (32 * c)) + kb * 32 * RC * 16);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32<T>(kf, qf[qb][c], s[qb][kb]);
       }
@@ -185,6 +193,10 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   const int vj = lane & 15, vq = lane >> 4;
   const int v_row0 = 8 * g + (vj >> 2);
   const int v_col = 16 * (vq & 1) + 4 * (vj & 3);
+  // V^T fragment (rows 16t + v_row0 + 4h, columns 32db + v_col): byte offset
+  // v_off[h] ^ (64 db), plus 16t rows as an immediate.
+  const uint32_t v_off0 = v_chunk<RC>(v_row0, v_col >> 3) * 16 + (v_col & 7) * 2;
+  const uint32_t v_off1 = v_chunk<RC>(v_row0 + 4, v_col >> 3) * 16 + (v_col & 7) * 2;
   const float c2 = a.scale_log2;
 
   // One position i of the tile sequence (key tile kt, its successors kt1
@@ -277,22 +289,70 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       }
     }
 
-    // Scores of the next tile (its K is resident) -- independent of the
-    // softmax below, so the two overlap.  On a wave's last tile the MFMAs
-    // read a stale buffer and the result is discarded.
-    scores(Knext, s_nxt);
+    // Scores of the next tile (its K is resident), software-pipelined with
+    // the exponentials of this tile: slice i issues the K read for score
+    // MFMA i + PK, score MFMA i, and 32/NS of the exponentials; a scheduling
+    // barrier closes each slice so the reads stay PK MFMAs ahead.  On a
+    // wave's last tile the score MFMAs read a stale buffer and the result is
+    // discarded.
+    {
+      constexpr int NS = 2 * (D / 16);  // score MFMAs per tile
+      constexpr int PK = 3;             // K fragments in flight
+      constexpr int EPI = 32 / NS;      // exponentials per slice and query block
+      const char* __restrict__ Kb = (const char*)Knext;
+      uint32_t kbase = k_off;
+      asm volatile("" : "+v"(kbase));
+      u32x4 kq[PK + 1];
+#pragma unroll
+      for (int i = 0; i < PK; ++i)
+        kq[i] = *(const u32x4*)(Kb + (kbase ^ (32 * (i >> 1))) + (i & 1) * 32 * RC * 16);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s_nxt[qb][0] = s_nxt[qb][1] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (i + PK < NS) {
+          const int j = i + PK;
+          kq[j % (PK + 1)] = *(const u32x4*)(Kb + (kbase ^ (32 * (j >> 1))) + (j & 1) * 32 * RC * 16);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s_nxt[qb][i & 1] = mfma32<T>(kq[i % (PK + 1)], qf[qb][i >> 1], s_nxt[qb][i & 1]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int e = 0; e < EPI; ++e) {
+            const int idx = i * EPI + e;
+            s[qb][idx >> 4][idx & 15] = fast_exp2(__builtin_fmaf(s[qb][idx >> 4][idx & 15], c2, -m_use[qb]));
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
 
-    // P = exp2(s*c2 - m), packed to fp16/bf16 (round to nearest even) as the
-    // B operand of O^T += V^T P^T.  For fp16 the row sum l adds the same
-    // rounded probabilities that weight V, pairwise in FP32 (v_dot2 with
-    // ones); bf16 keeps only 8 bits, so there l sums the FP32 values.
+    // V^T fragments of O^T += V^T P^T run PV reads ahead of their MFMAs;
+    // the first ones are issued before P is packed.
+    constexpr int NV = (BN / 16) * (D / 32);  // P V MFMAs per tile
+    constexpr int PV = 2;
+    const char* __restrict__ Vl = (const char*)Vcur;
+    uint32_t vb0 = v_off0, vb1 = v_off1;
+    asm volatile("" : "+v"(vb0), "+v"(vb1));
+    auto vread = [&](int i) {
+      const int t = i / (D / 32), db = i % (D / 32);
+      const u32x2 lo = lds_read_tr16(Vl + (vb0 ^ (64 * db)) + t * 16 * RC * 16);
+      const u32x2 hi = lds_read_tr16(Vl + (vb1 ^ (64 * db)) + t * 16 * RC * 16);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 vq[PV + 1];
+#pragma unroll
+    for (int i = 0; i < PV; ++i) vq[i] = vread(i);
+
+    // P = exp2(s*c2 - m) (computed above), packed to fp16/bf16 (round to
+    // nearest even) as the B operand of O^T += V^T P^T.  For fp16 the row
+    // sum l adds the same rounded probabilities that weight V, pairwise in
+    // FP32 (v_dot2 with ones); bf16 keeps only 8 bits, so there l sums the
+    // FP32 values.
     u32x4 pf[QB][BN / 16];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(__builtin_fmaf(s[qb][kb][r], c2, -m_use[qb]));
       if constexpr (DROP) {
         // l sums the undropped FP32 probabilities; then the dropped ones are
         // zeroed before packing (the keep scale is applied to O at the end).
@@ -328,23 +388,18 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       }
       l_run[qb] += lsum;
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T P^T, 16 keys per step: step t uses keys 16t .. 16t+15, which
     // are accumulator registers 8*(t%2) .. +7 of block t/2 (see acc_row).
     // Each V^T fragment feeds the QB query blocks.
-    const char* __restrict__ Vl = (const char*)Vcur;
 #pragma unroll
-    for (int t = 0; t < BN / 16; ++t) {
+    for (int i = 0; i < NV; ++i) {
+      if (i + PV < NV) vq[(i + PV) % (PV + 1)] = vread(i + PV);
+      const int t = i / (D / 32), db = i % (D / 32);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int col = db * 32 + v_col;
-        const int r0 = 16 * t + v_row0;
-        const u32x2 lo = lds_read_tr16(Vl + v_chunk<RC>(r0, col >> 3) * 16 + (col & 7) * 2);
-        const u32x2 hi = lds_read_tr16(Vl + v_chunk<RC>(r0 + 4, col >> 3) * 16 + (col & 7) * 2);
-        const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<T>(vf, pf[qb][t], oacc[qb][db]);
-      }
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<T>(vq[i % (PV + 1)], pf[qb][t], oacc[qb][db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
