@@ -154,9 +154,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   constexpr int RC = D / 8, TC = BQ * RC;
   __shared__ u32x4 lq0[TC], lq1[TC], lg0[TC], lg1[TC];
   __shared__ __attribute__((aligned(16))) float ll0[BQ], ll1[BQ], ld0[BQ], ld1[BQ];
-  // Dropout: per wave, 32 words (one per query of the block); bits 0-15
-  // keys k0w..k0w+15, bits 16-31 keys k0w+16..k0w+31.
-  __shared__ __attribute__((aligned(16))) uint32_t drop_w[DROP ? kThreads / 64 : 1][32];
+  // Dropout: per wave and 32-query block, 32 words (one per query); bits
+  // 0-15 keys k0w..k0w+15, bits 16-31 keys k0w+16..k0w+31.
+  __shared__ __attribute__((aligned(16))) uint32_t drop_w[DROP ? kThreads / 64 : 1][2][32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -209,17 +209,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   // LDS byte offsets (see fwd): row reads of query row qb*32 + perm23(l32),
   // chunk 2c + g; transposed reads of rows qb*32 + 16*t2 + 8g + j/4 (+4),
   // columns 32db + 16(q%2) + 4(j%4).  Whole 16-row steps are immediates.
-  int roff[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) roff[c] = dual_chunk<RC>(perm23(l32), 2 * c + g) * 16;
+  // The dual swizzle XORs only chunk bits below the row, so the row read of
+  // chunk 2c + g is roff0 ^ (32c) and the transposed read of columns 32db +
+  // ... is toff[h] ^ (64db); whole 16-row steps are immediates.
+  const uint32_t roff0 = dual_chunk<RC>(perm23(l32), g) * 16;
   const int vj = lane & 15, vq = lane >> 4;
   const int t_row0 = 8 * g + (vj >> 2);
   const int t_col = 16 * (vq & 1) + 4 * (vj & 3);
-  int toff[D / 32][2];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) toff[db][h] = tr_offset<RC>(t_row0 + 4 * h, db * 32 + t_col);
+  const uint32_t toff0 = tr_offset<RC>(t_row0, t_col), toff1 = tr_offset<RC>(t_row0 + 4, t_col);
   constexpr int ROW16 = 16 * RC * 16;  // bytes of 16 rows
 
   const int src0 = tile_src_offset<D, true>(wave * 64 + lane);
@@ -246,7 +243,185 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     }
   };
 
-  auto compute = [&](int j, int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
+  // One 64-query tile = two 32-query blocks, as a software pipeline of four
+  // stages whose slices pair one MFMA with one LDS read (kept PR reads
+  // ahead) and a share of the vector work, closed by scheduling barriers:
+  //   1. S, dP of block 0              (row reads of Q and dO)
+  //   2. S, dP of block 1  | P, dS of block 0
+  //   3. dV, dK of block 0 | P, dS of block 1   (transposed reads of dO, Q)
+  //   4. dV, dK of block 1
+  // A block wholly before this wave's keys (causal) is computed and masked
+  // to zero rather than skipped, which keeps the pipeline uniform; it only
+  // occurs on diagonal tiles.
+  constexpr int DB = D / 32;
+  constexpr int N1 = 2 * (D / 16);  // S + dP MFMAs per block
+  constexpr int N3 = 4 * DB;        // dV + dK MFMAs per block
+  constexpr int E1 = 16 / N1 > 0 ? (16 + N1 - 1) / N1 : 1;  // softmax elements per slice
+  constexpr int PR = 3;             // row reads in flight
+  constexpr int PT = 2;             // transposed read pairs in flight
+  auto compute_pipe = [&](int j, int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
+    const char* Qb = (const char*)Ql;
+    const char* Gb = (const char*)Gl;
+    const int q0 = qt * BQ;
+    uint32_t rb = roff0, tb0 = toff0, tb1 = toff1;
+    asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));
+    // row fragment m of the tile: block m / N1; within it, n even -> Q chunk
+    // n/2 (S), n odd -> dO chunk n/2 (dP)
+    auto row_frag = [&](int m) {
+      const int qb = m / N1, n = m % N1;
+      return *(const u32x4*)(((n & 1) ? Gb : Qb) + qb * 2 * ROW16 + (rb ^ (32 * (n >> 1))));
+    };
+    // transposed fragment m: block m / N3; n = (t2*DB + db)*2 + w, w = 0 -> dO^T (dV), 1 -> Q^T (dK)
+    auto tr_frag = [&](int m) {
+      const int qb = m / N3, n = m % N3;
+      const int w = n & 1, db = (n >> 1) % DB, t2 = (n >> 1) / DB;
+      const char* base = (w ? Qb : Gb) + (qb * 2 + t2) * ROW16;
+      const u32x2 lo = lds_read_tr16(base + (tb0 ^ (64 * db)));
+      const u32x2 hi = lds_read_tr16(base + (tb1 ^ (64 * db)));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    f32x16 s[2], dp[2];
+    float lse_r[2][16], dl_r[2][16];
+    uint32_t kbits[2] = {0xffffffffu, 0xffffffffu};  // dropout keep bit r: query qb0 + acc_row(r, g)
+    if constexpr (DROP) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const uint32_t row_bits = dropout_bits16(k0w / 16 + g, q0 + qb * 32 + l32, (uint64_t)(bhk * G + j),
+                                                 a.drop.seed, a.drop.offset, a.drop.thr);
+        ((uint16_t*)&drop_w[wave][qb][l32])[g] = (uint16_t)row_bits;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS ops run in order
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const u32x4* wv = (const u32x4*)&drop_w[wave][qb][0];
+        const u32x4 w0 = wv[2 * g], w1 = wv[2 * g + 1], w2 = wv[4 + 2 * g], w3 = wv[5 + 2 * g];
+        const uint32_t wq[16] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
+                                 w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
+        uint32_t b = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) b |= ((wq[r] >> l32) & 1u) << r;
+        kbits[qb] = b;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next tile rewrites it
+    }
+    // LSE (x log2 e) and Delta of the rows a lane's registers hold: register
+    // r of block qb is query qb*32 + acc_row(r, g), two runs of 8.
+    auto load_rows = [&](int qb) {
+      const f32x4* lse4 = (const f32x4*)ll;
+      const f32x4* dl4 = (const f32x4*)ld;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v4 = 0; v4 < 2; ++v4) {
+          const int idx = (qb * 32 + h * 16 + g * 8) / 4 + v4;
+          const f32x4 x = lse4[idx], y = dl4[idx];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lse_r[qb][h * 8 + v4 * 4 + e] = x[e];
+            dl_r[qb][h * 8 + v4 * 4 + e] = y[e];
+          }
+        }
+    };
+    // Causal mask of block qb on its raw scores (-inf), only where the block
+    // meets the diagonal (a uniform test), before its exponentials.
+    auto mask_block = [&](int qb) {
+      const int qb0 = q0 + qb * 32;
+      if (CAUSAL && qb0 < k0w + 31) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (my_k > qb0 + acc_row(r, g)) s[qb][r] = -INFINITY;
+      }
+    };
+    // P and dS of element r of block qb (in place in s, dp)
+    const float ks = DROP ? a.drop.keep_scale : 1.f;
+    auto softmax_elem = [&](int qb, int r) {
+      const float p = fast_exp2(__builtin_fmaf(s[qb][r], c2, -lse_r[qb][r]));
+      if constexpr (DROP) {
+        const bool keep = (kbits[qb] >> r) & 1u;
+        s[qb][r] = keep ? p * ks : 0.f;                        // dropped, scaled P for dV
+        dp[qb][r] = p * ((keep ? dp[qb][r] * ks : 0.f) - dl_r[qb][r]);  // dS
+      } else {
+        s[qb][r] = p;
+        dp[qb][r] = p * (dp[qb][r] - dl_r[qb][r]);
+      }
+    };
+    u32x4 pf[2][2], sf[2][2];
+    auto pack_block = [&](int qb) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        pf[qb][t2] = pack8<T>(s[qb], t2 * 8);
+        sf[qb][t2] = pack8<T>(dp[qb], t2 * 8);
+      }
+    };
+    auto mfma1 = [&](int m, u32x4 f) {  // S or dP MFMA m of the tile
+      const int qb = m / N1, n = m % N1;
+      if (n & 1) dp[qb] = mfma32<T>(f, vf[n >> 1], dp[qb]);
+      else s[qb] = mfma32<T>(f, kf[n >> 1], s[qb]);
+    };
+    auto mfma3 = [&](int m, u32x4 f) {  // dV or dK MFMA m of the tile
+      const int qb = m / N3, n = m % N3;
+      const int w = n & 1, db = (n >> 1) % DB, t2 = (n >> 1) / DB;
+      if (w) dk[db] = mfma32<T>(f, sf[qb][t2], dk[db]);
+      else dv[db] = mfma32<T>(f, pf[qb][t2], dv[db]);
+    };
+
+    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+    u32x4 rq[PR + 1];
+#pragma unroll
+    for (int m = 0; m < PR; ++m) rq[m] = row_frag(m);
+    // stage 1: S, dP of block 0
+#pragma unroll
+    for (int m = 0; m < N1; ++m) {
+      rq[(m + PR) % (PR + 1)] = row_frag(m + PR);
+      if (m == 1) load_rows(0);
+      mfma1(m, rq[m % (PR + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mask_block(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 2: S, dP of block 1 | P, dS of block 0
+#pragma unroll
+    for (int m = N1; m < 2 * N1; ++m) {
+      if (m + PR < 2 * N1) rq[(m + PR) % (PR + 1)] = row_frag(m + PR);
+      if (m == N1 + 1) load_rows(1);
+      mfma1(m, rq[m % (PR + 1)]);
+#pragma unroll
+      for (int e = 0; e < E1; ++e)
+        if ((m - N1) * E1 + e < 16) softmax_elem(0, (m - N1) * E1 + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pack_block(0);
+    mask_block(1);
+    u32x4 tq[PT + 1];
+#pragma unroll
+    for (int m = 0; m < PT; ++m) tq[m] = tr_frag(m);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 3: dV, dK of block 0 | P, dS of block 1
+    constexpr int E3 = (16 + N3 - 1) / N3;
+#pragma unroll
+    for (int m = 0; m < N3; ++m) {
+      tq[(m + PT) % (PT + 1)] = tr_frag(m + PT);
+      mfma3(m, tq[m % (PT + 1)]);
+#pragma unroll
+      for (int e = 0; e < E3; ++e)
+        if (m * E3 + e < 16) softmax_elem(1, m * E3 + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pack_block(1);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 4: dV, dK of block 1
+#pragma unroll
+    for (int m = N3; m < 2 * N3; ++m) {
+      if (m + PT < 2 * N3) tq[(m + PT) % (PT + 1)] = tr_frag(m + PT);
+      mfma3(m, tq[m % (PT + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // D = 64: the same work one 32-query block at a time, leaving the
+  // schedule to the compiler -- the pipelined form needs more registers
+  // there and costs one wave per SIMD of occupancy, which measures slower.
+  auto compute_blocks = [&](int j, int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
     const char* Qb = (const char*)Ql;
     const char* Gb = (const char*)Gl;
     const int q0 = qt * BQ;
@@ -257,8 +432,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        s = mfma32<T>(*(const u32x4*)(Qb + qb * 2 * ROW16 + roff[c]), kf[c], s);
-        dp = mfma32<T>(*(const u32x4*)(Gb + qb * 2 * ROW16 + roff[c]), vf[c], dp);
+        s = mfma32<T>(*(const u32x4*)(Qb + qb * 2 * ROW16 + (roff0 ^ (32 * c))), kf[c], s);
+        dp = mfma32<T>(*(const u32x4*)(Gb + qb * 2 * ROW16 + (roff0 ^ (32 * c))), vf[c], dp);
       }
       // Register r holds query qb*32 + acc_row(r, g): two runs of 8.
       const f32x4* lse4 = (const f32x4*)ll;
@@ -277,33 +452,32 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
           }
         }
       const bool diag = CAUSAL && qb0 < k0w + 31;
+      uint32_t kbits = 0xffffffffu;
       if constexpr (DROP) {
-        // this lane's Philox block: query qb0 + l32, keys k0w + 16g .. +15
         const uint32_t row_bits = dropout_bits16(k0w / 16 + g, qb0 + l32, (uint64_t)(bhk * G + j), a.drop.seed,
                                                  a.drop.offset, a.drop.thr);
         asm volatile("" ::: "memory");
-        ((uint16_t*)&drop_w[wave][l32])[g] = (uint16_t)row_bits;
+        ((uint16_t*)&drop_w[wave][0][l32])[g] = (uint16_t)row_bits;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS ops run in order
-        // register r holds query qb0 + acc_row(r, g): words 8g .. 8g+7, 16+8g .. 16+8g+7
-        const u32x4* wv = (const u32x4*)&drop_w[wave][0];
+        const u32x4* wv = (const u32x4*)&drop_w[wave][0][0];
         const u32x4 w0 = wv[2 * g], w1 = wv[2 * g + 1], w2 = wv[4 + 2 * g], w3 = wv[5 + 2 * g];
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next block rewrites it
         const uint32_t wq[16] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
                                  w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
-        const float ks = a.drop.keep_scale;
+        kbits = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[r], c2, -lse_r[r]));
-          if (diag && my_k > qb0 + acc_row(r, g)) p = 0.f;
-          const bool keep = (wq[r] >> l32) & 1u;
-          s[r] = keep ? p * ks : 0.f;                     // dropped, scaled P for dV
+        for (int r = 0; r < 16; ++r) kbits |= ((wq[r] >> l32) & 1u) << r;
+      }
+      const float ks = DROP ? a.drop.keep_scale : 1.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[r], c2, -lse_r[r]));
+        if (diag && my_k > qb0 + acc_row(r, g)) p = 0.f;
+        if constexpr (DROP) {
+          const bool keep = (kbits >> r) & 1u;
+          s[r] = keep ? p * ks : 0.f;                         // dropped, scaled P for dV
           dp[r] = p * ((keep ? dp[r] * ks : 0.f) - dl_r[r]);  // dS
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[r], c2, -lse_r[r]));
-          if (diag && my_k > qb0 + acc_row(r, g)) p = 0.f;
+        } else {
           s[r] = p;
           dp[r] = p * (dp[r] - dl_r[r]);
         }
@@ -315,15 +489,19 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
         const int rows = (qb * 2 + t2) * ROW16;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const u32x2 glo = lds_read_tr16(Gb + rows + toff[db][0]);
-          const u32x2 ghi = lds_read_tr16(Gb + rows + toff[db][1]);
+          const u32x2 glo = lds_read_tr16(Gb + rows + (toff0 ^ (64 * db)));
+          const u32x2 ghi = lds_read_tr16(Gb + rows + (toff1 ^ (64 * db)));
           dv[db] = mfma32<T>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pf, dv[db]);
-          const u32x2 qlo = lds_read_tr16(Qb + rows + toff[db][0]);
-          const u32x2 qhi = lds_read_tr16(Qb + rows + toff[db][1]);
+          const u32x2 qlo = lds_read_tr16(Qb + rows + (toff0 ^ (64 * db)));
+          const u32x2 qhi = lds_read_tr16(Qb + rows + (toff1 ^ (64 * db)));
           dk[db] = mfma32<T>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sf, dk[db]);
         }
       }
     }
+  };
+  auto compute = [&](int j, int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
+    if constexpr (D == 128) compute_pipe(j, qt, Ql, Gl, ll, ld);
+    else compute_blocks(j, qt, Ql, Gl, ll, ld);
   };
 
   // The workgroup walks positions p = 0 .. n_pos-1, position p being query
@@ -470,23 +648,13 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
 
   // LDS byte offsets: K rows (dual swizzle) and V rows (swz) of key
-  // kb*32 + perm23(ql), chunk 2c + g; transposed K reads of rows
-  // 16t + 8g + j/4 (+4), columns 32db + 16(q%2) + 4(j%4).
+  // kb*32 + perm23(ql), chunk 2c + g are koff0 / voff0 ^ (32c); transposed
+  // K reads of rows 16t + 8g + j/4 (+4), columns 32db + 16(q%2) + 4(j%4) are
+  // toff0 / toff1 ^ (64db) (the swizzles XOR only chunk bits below the row).
   const int krow = perm23(ql);
-  int koff[D / 16], voff[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    koff[c] = dual_chunk<RC>(krow, 2 * c + g) * 16;
-    voff[c] = swz(krow * RC + 2 * c + g) * 16;
-  }
   const int vj = lane & 15, vq = lane >> 4;
   const int t_row0 = 8 * g + (vj >> 2);
   const int t_col = 16 * (vq & 1) + 4 * (vj & 3);
-  int toff[D / 32][2];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) toff[db][h] = tr_offset<RC>(t_row0 + 4 * h, db * 32 + t_col);
   constexpr int ROW16 = 16 * RC * 16;
 
   const int ksrc0 = tile_src_offset<D, true>(wave * 64 + lane);
@@ -495,65 +663,121 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const int n_kt = CAUSAL ? min(n_kt_all, ((qt + 1) * BM) / BN) : n_kt_all;
   const float c2 = a.scale_log2;
 
+  // One 64-key tile as a software pipeline of four stages whose slices pair
+  // one MFMA with one LDS read (kept PR ahead) and a share of the vector
+  // work, closed by scheduling barriers:
+  //   1. S^T, dP^T of keys 0-31                     (row reads of K and V)
+  //   2. S^T, dP^T of keys 32-63 | P, dS of keys 0-31
+  //   3. dQ^T += K^T dS^T, keys 0-31 | P, dS of keys 32-63  (transposed K reads)
+  //   4. dQ^T += K^T dS^T, keys 32-63
+  // Masks (causal diagonal, partial last tile, partly visible tile) set the
+  // raw scores of a 32-key block to -inf between stages, in a uniform branch.
+  constexpr int DB = D / 32;
+  constexpr int N1 = 2 * (D / 16);  // S + dP MFMAs per 32-key block
+  constexpr int N3 = 2 * DB;        // dQ MFMAs per 32-key block
+  constexpr int PR = 3, PT = 2;
+  const uint32_t koff0 = dual_chunk<RC>(krow, g) * 16, voff0 = swz(krow * RC + g) * 16;
+  const uint32_t toff0 = tr_offset<RC>(t_row0, t_col), toff1 = tr_offset<RC>(t_row0 + 4, t_col);
   auto compute = [&](int kt, uint32_t wlo, uint32_t whi, const u32x4* Kl, const u32x4* Vl) {
     const char* Kb = (const char*)Kl;
     const char* Vb = (const char*)Vl;
     const int k0 = kt * BN;
+    uint32_t kb_ = koff0, vb_ = voff0, tb0 = toff0, tb1 = toff1;
+    asm volatile("" : "+v"(kb_), "+v"(vb_), "+v"(tb0), "+v"(tb1));
+    // row fragment m: block m / N1; n even -> K chunk n/2 (S^T), odd -> V chunk n/2 (dP^T)
+    auto row_frag = [&](int m) {
+      const int kb = m / N1, n = m % N1;
+      return (n & 1) ? *(const u32x4*)(Vb + kb * 2 * ROW16 + (vb_ ^ (32 * (n >> 1))))
+                     : *(const u32x4*)(Kb + kb * 2 * ROW16 + (kb_ ^ (32 * (n >> 1))));
+    };
+    // transposed K fragment m: 16-key step t = m / DB, column block db = m % DB
+    auto tr_frag = [&](int m) {
+      const int t = m / DB, db = m % DB;
+      const u32x2 lo = lds_read_tr16(Kb + t * ROW16 + (tb0 ^ (64 * db)));
+      const u32x2 hi = lds_read_tr16(Kb + t * ROW16 + (tb1 ^ (64 * db)));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s[kb] = mfma32<T>(*(const u32x4*)(Kb + kb * 2 * ROW16 + koff[c]), qf[c], s[kb]);
-        dp[kb] = mfma32<T>(*(const u32x4*)(Vb + kb * 2 * ROW16 + voff[c]), gf[c], dp[kb]);
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c2, -lse2));
-    // Diagonal tile, partial last tile (keys >= N do not exist) or partially
-    // visible tile: zero the masked probabilities.  The test is uniform, so
-    // other tiles skip it.
-    const bool partial = MASK ? (wlo & whi) != 0xffffffffu : k0 + BN > N;
-    if ((CAUSAL && k0 + BN - 1 > q0w) || partial) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    const bool need_mask = (CAUSAL && k0 + BN - 1 > q0w) || (MASK ? (wlo & whi) != 0xffffffffu : k0 + BN > N);
+    auto mask_block = [&](int kb) {
+      if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + acc_row(r, g);
           const bool hidden = MASK ? key_hidden(wlo, whi, kb, r, g) : key >= N;
-          if ((CAUSAL && key > my_q) || hidden) s[kb][r] = 0.f;
+          if ((CAUSAL && key > my_q) || hidden) s[kb][r] = -INFINITY;
         }
-    }
-    if constexpr (DROP) {
-      const float ks = a.drop.keep_scale;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t keep = dropout_bits_st(k0 + kb * 32, my_q, (uint64_t)bh, a.drop.seed, a.drop.offset,
-                                              a.drop.thr, g);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          dp[kb][r] = s[kb][r] * ((((keep >> r) & 1u) ? dp[kb][r] * ks : 0.f) - dl);
       }
-    } else {
+    };
+    uint32_t keep[2] = {0xffffffffu, 0xffffffffu};
+    if constexpr (DROP) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[kb][r] = s[kb][r] * (dp[kb][r] - dl);
+        keep[kb] = dropout_bits_st(k0 + kb * 32, my_q, (uint64_t)bh, a.drop.seed, a.drop.offset, a.drop.thr, g);
     }
-    // dQ^T += K^T dS^T, 16 keys per step (registers 8*(t%2).. of block t/2).
+    const float ks = DROP ? a.drop.keep_scale : 1.f;
+    auto softmax_elem = [&](int kb, int r) {
+      const float p = fast_exp2(__builtin_fmaf(s[kb][r], c2, -lse2));
+      if constexpr (DROP) dp[kb][r] = p * ((((keep[kb] >> r) & 1u) ? dp[kb][r] * ks : 0.f) - dl);
+      else dp[kb][r] = p * (dp[kb][r] - dl);
+    };
+    u32x4 sf[BN / 16];
+    auto pack_block = [&](int kb) {
+      sf[2 * kb] = pack8<T>(dp[kb], 0);
+      sf[2 * kb + 1] = pack8<T>(dp[kb], 8);
+    };
+    auto mfma1 = [&](int m, u32x4 f) {
+      const int kb = m / N1, n = m % N1;
+      if (n & 1) dp[kb] = mfma32<T>(f, gf[n >> 1], dp[kb]);
+      else s[kb] = mfma32<T>(f, qf[n >> 1], s[kb]);
+    };
+    auto mfma3 = [&](int m, u32x4 f) { dq[m % DB] = mfma32<T>(f, sf[m / DB], dq[m % DB]); };
+
+    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+    u32x4 rq[PR + 1];
 #pragma unroll
-    for (int t = 0; t < BN / 16; ++t) {
-      const u32x4 sf = pack8<T>(dp[t >> 1], (t & 1) * 8);
+    for (int m = 0; m < PR; ++m) rq[m] = row_frag(m);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const u32x2 lo = lds_read_tr16(Kb + t * ROW16 + toff[db][0]);
-        const u32x2 hi = lds_read_tr16(Kb + t * ROW16 + toff[db][1]);
-        dq[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf, dq[db]);
-      }
+    for (int m = 0; m < N1; ++m) {  // stage 1
+      rq[(m + PR) % (PR + 1)] = row_frag(m + PR);
+      mfma1(m, rq[m % (PR + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mask_block(0);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int E1 = (16 + N1 - 1) / N1;
+#pragma unroll
+    for (int m = N1; m < 2 * N1; ++m) {  // stage 2
+      if (m + PR < 2 * N1) rq[(m + PR) % (PR + 1)] = row_frag(m + PR);
+      mfma1(m, rq[m % (PR + 1)]);
+#pragma unroll
+      for (int e = 0; e < E1; ++e)
+        if ((m - N1) * E1 + e < 16) softmax_elem(0, (m - N1) * E1 + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pack_block(0);
+    mask_block(1);
+    u32x4 tq[PT + 1];
+#pragma unroll
+    for (int m = 0; m < PT; ++m) tq[m] = tr_frag(m);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int E3 = (16 + N3 - 1) / N3;
+#pragma unroll
+    for (int m = 0; m < N3; ++m) {  // stage 3
+      tq[(m + PT) % (PT + 1)] = tr_frag(m + PT);
+      mfma3(m, tq[m % (PT + 1)]);
+#pragma unroll
+      for (int e = 0; e < E3; ++e)
+        if (m * E3 + e < 16) softmax_elem(1, m * E3 + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pack_block(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = N3; m < 2 * N3; ++m) {  // stage 4
+      if (m + PT < 2 * N3) tq[(m + PT) % (PT + 1)] = tr_frag(m + PT);
+      mfma3(m, tq[m % (PT + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
