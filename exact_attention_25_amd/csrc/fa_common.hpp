@@ -103,14 +103,20 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& s, int lo) {
 __device__ __forceinline__ int swz(int chunk) { return chunk ^ ((chunk >> 4) & 15); }
 
 // Chunk swizzle for a tile (RC 16-byte chunks per row) that is read both by
-// rows (16 lanes, 16 different rows, same logical chunk, ds_read_b128) and
-// transposed (ds_read_b64_tr_b16: 4 consecutive rows x 2 adjacent chunks per
-// 16-lane group).  The XOR value takes 16 (RC = 16) or, per row parity, 8
-// distinct values over 16 consecutive rows and 4 distinct values with equal
-// low bit over 4 aligned rows, so both patterns hit distinct banks.
+// rows (ds_read_b128, served 16 lanes at a time: 16 different rows, same
+// logical chunk) and transposed (ds_read_b64_tr_b16, served 32 lanes at a
+// time: 4 consecutive aligned rows x 4 adjacent chunks).  With 64 banks of 4
+// bytes a 256-byte line holds 16 chunk positions.  RC = 16 (one row per
+// line): the XOR value 4*(r%4) + (r/4)%4 takes all 16 values over 16
+// consecutive rows, and over 4 aligned rows its bits 2-3 differ, so the
+// 4 x 4 chunks of a transposed read land on 16 distinct positions.  RC = 8
+// (two rows per line, odd rows in the upper half): 4*((r/2)%2) + (r/4)%4
+// takes 8 distinct values on the even and on the odd rows of 16 consecutive
+// rows, and differs in bit 2 between the two even (or odd) rows of 4
+// aligned rows.  Both depend only on the low four bits of the row.
 template <int RC>
 __device__ __forceinline__ int dual_xor(int r) {
-  return RC == 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+  return RC == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 template <int RC>
 __device__ __forceinline__ int dual_chunk(int r, int c) {

@@ -22,15 +22,22 @@
 //  * Keys and values stream in tiles of 64 keys straight from HBM into a
 //    double-buffered LDS ring (buffer_load_dwordx4 ... lds: no VGPR staging), one
 //    workgroup barrier per tile.  Both tiles stay row-major with an XOR
-//    swizzle of 16-byte chunks; K fragments are read with ds_read_b128 and
-//    the V^T fragments of O^T = V^T P^T with the transposing
-//    ds_read_b64_tr_b16, so V is never transposed in memory.
+//    swizzle of 16-byte chunks (K: swz, V: dual_chunk, each conflict-free
+//    for its read); K fragments are read with ds_read_b128 and the V^T
+//    fragments of O^T = V^T P^T with the transposing ds_read_b64_tr_b16, so
+//    V is never transposed in memory.
 //  * Computing S^T puts one query per lane (two lanes per query, 32 keys
 //    each), so the row max is an in-lane reduction plus one cross-half swap,
 //    and the row sum needs no cross-lane step until the epilogue.
-//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  While
-//    the softmax of tile j runs, the score MFMAs of tile j+1 are issued (K
-//    streams one tile ahead of V), so matrix and vector work overlap.
+//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  Every
+//    matrix instruction has vector work beside it: the exponentials of tile
+//    j run between the score MFMAs of tile j+1 (K streams one tile ahead of
+//    V), and the packing of tile j's probabilities and the row max of tile
+//    j+1 run between the P V MFMAs of tile j.  On gfx950 an MFMA holds the
+//    vector issue port only for part of its duration, so vector work placed
+//    this way is largely hidden, and what is left is bounded by the count of
+//    vector instructions per tile; the loop keeps that count low (read
+//    offsets held in registers, a one-compare rescale decision).
 //  * Workgroups are numbered heaviest-first for causal masks, and all query
 //    tiles of one head get workgroup ids congruent modulo 8, so they run on
 //    the same XCD and share its L2 for the re-streamed K/V.
@@ -50,15 +57,6 @@ constexpr int kFwdQB = 1;
 constexpr int kFwdThreads = 256;
 constexpr float kLazy = 8.0f;          // max probability 2^8 between rescales
 constexpr float kFastLimit = 4096.0f;  // |scale*log2e*S| below this: one-FMA exponent
-
-// Physical 16-byte-chunk index of (row r, chunk c) in a V tile with RC chunks
-// per row.  The XOR uses even values 2*(r & m), so the four consecutive rows
-// and two adjacent chunks touched by one 16-lane transposed read land on
-// eight distinct chunk positions (no bank conflicts).
-template <int RC>
-__device__ __forceinline__ int v_chunk(int r, int c) {
-  return r * RC + (c ^ ((r & (RC == 16 ? 7 : 3)) << 1));
-}
 
 template <int QB>
 struct FwdShape {
@@ -153,7 +151,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   const int p0 = wave * 64 + lane;
   const int ksrc0 = swz(p0) * 8;
   const int vr0 = p0 / RC;
-  const int vsrc0 = vr0 * D + ((p0 % RC) ^ ((vr0 & (RC == 16 ? 7 : 3)) << 1)) * 8;
+  const int vsrc0 = vr0 * D + ((p0 % RC) ^ dual_xor<RC>(vr0)) * 8;
   auto load_k = [&](int kt, u32x4* dst) {
     copy_tile_rows<D, LPT, NT>(Kh + (int64_t)kt * BN * D, ksrc0, dst + wave * 64, min(BN, (int)N - kt * BN));
   };
@@ -195,33 +193,29 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   const int v_col = 16 * (vq & 1) + 4 * (vj & 3);
   // V^T fragment (rows 16t + v_row0 + 4h, columns 32db + v_col): byte offset
   // v_off[h] ^ (64 db), plus 16t rows as an immediate.
-  const uint32_t v_off0 = v_chunk<RC>(v_row0, v_col >> 3) * 16 + (v_col & 7) * 2;
-  const uint32_t v_off1 = v_chunk<RC>(v_row0 + 4, v_col >> 3) * 16 + (v_col & 7) * 2;
+  const uint32_t v_off0 = dual_chunk<RC>(v_row0, v_col >> 3) * 16 + (v_col & 7) * 2;
+  const uint32_t v_off1 = dual_chunk<RC>(v_row0 + 4, v_col >> 3) * 16 + (v_col & 7) * 2;
+  // All chunk-XORed read offsets stay in registers for the whole pass (they
+  // differ only by XORs with constants, so they are formed once here).
+  uint32_t k_addr[RC / 2], v_addr[2][D / 32];
+#pragma unroll
+  for (int c = 0; c < RC / 2; ++c) k_addr[c] = k_off ^ (32 * c);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    v_addr[0][db] = v_off0 ^ (64 * db);
+    v_addr[1][db] = v_off1 ^ (64 * db);
+  }
   const float c2 = a.scale_log2;
 
-  // One position i of the tile sequence (key tile kt, its successors kt1
-  // and kt2 at positions i+1 and i+2), software-pipelined: on entry s holds
-  // the raw scores of tile kt (computed during the previous step); while the
-  // softmax of tile kt runs on the vector ALUs, the score MFMAs of tile kt1
-  // (its K is already in LDS) are issued into s_nxt.  K therefore streams
-  // one tile ahead of V: the copies started here are K of tile kt2 (into the
-  // buffer that held K of tile kt) and V of tile kt1.  wlo/whi: visibility
-  // word of tile kt (mask mode).
-  auto step = [&](int i, int kt, int kt1, int kt2, uint32_t wlo, uint32_t whi, const u32x4* __restrict__ Knext,
-                  const u32x4* __restrict__ Vcur, u32x4* kdst, u32x4* vdst, f32x16 (&s)[QB][2],
-                  f32x16 (&s_nxt)[QB][2]) {
-    wait_vmem();      // K of tile kt1 and V of tile kt have landed (this wave's part)
-    __syncthreads();  // ... everyone's part; everyone is done with the previous tile
-    if (i + 2 < i_end) load_k(kt2, kdst);
-    if (i + 1 < i_end) load_v(kt1, vdst);
+  // Raw max over the tile of the pending scores, per query row; carried from
+  // the step that computed those scores to the step that exponentiates them.
+  float mx[QB];
 
-    const int k0 = kt * BN;
-    if (!active || (CAUSAL && k0 > q0w + WQ - 1)) return;  // nothing visible
-
-    // Diagonal tile, partial last tile or partially visible tile: mask
-    // before the max (a block wholly above its queries is masked entirely
-    // and contributes zero probabilities; keys >= N do not exist).  The
-    // tests are uniform, so other tiles take no per-element branch.
+  // Mask of a tile's raw scores before its max: diagonal, partial last or
+  // partially visible tiles only (a block wholly above its queries is masked
+  // entirely and contributes zero probabilities; keys >= N do not exist).
+  // The tests are uniform, so other tiles take no per-element branch.
+  auto mask_tile = [&](f32x16 (&s)[QB][2], int k0, uint32_t wlo, uint32_t whi) __attribute__((always_inline)) {
     const bool partial = MASK ? (wlo & whi) != 0xffffffffu : k0 + BN > N;
     if ((CAUSAL && k0 + BN - 1 > q0w) || partial) {
 #pragma unroll
@@ -235,19 +229,8 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
             if ((CAUSAL && key > q0w + 32 * qb + ql) || hidden) s[qb][kb][r] = -INFINITY;
           }
     }
-
-    // The reference max r_raw is always one of the raw scores (exact).  In
-    // the usual case the exponent is one FMA, s*c2 - RN(r_raw*c2), and the
-    // reference is only raised when the tile max exceeds it by more than
-    // kLazy in log2 units, so probabilities stay below 2^kLazy and the O/l
-    // rescale is skipped on most tiles; the result is unchanged because O
-    // and l always share the same reference.  When scaled scores are so
-    // large that RN(r_raw*c2) is off by a meaningful amount
-    // (|.| >= kFastLimit), the scores are first shifted by r_raw in raw
-    // units, where the difference is exact for scores near the max, and the
-    // same FMA then scales them.
-    float mx[QB], mref[QB];
-    bool fast_ok = true, need = false;
+  };
+  auto tile_max = [&](const f32x16 (&s)[QB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float m = s[qb][0][0];
@@ -255,37 +238,93 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, s[qb][1][r]);
-      mx[qb] = xhalf_max(m);  // raw max of this row over the tile
-      const float mc_tile = mx[qb] * c2;
-      mref[qb] = r_raw[qb] * c2;
-      fast_ok = fast_ok && (fabsf(mc_tile) < kFastLimit || mc_tile == -INFINITY) &&
-                (fabsf(mref[qb]) < kFastLimit || mref[qb] == -INFINITY);
-      need = need || (mc_tile > mref[qb] + kLazy);
+      mx[qb] = xhalf_max(m);
     }
-    const bool exact = !wave_all(fast_ok);
-    if (exact || wave_any(need)) {
+  };
+
+  // Reference state.  The reference max r_raw is always one of the raw
+  // scores (exact); mref = RN(r_raw*c2), m_use the same with -inf read as 0,
+  // mlazy = mref + kLazy.  In the usual case the exponent is one FMA,
+  // s*c2 - mref, and the reference is only raised (d_rescale) when a tile's
+  // max exceeds it by more than kLazy in log2 units, so probabilities stay
+  // below 2^kLazy and the O/l rescale is skipped on most tiles; the result is
+  // unchanged because O and l always share the same reference.  When the
+  // reference of some row of the wave is so large that RN(r_raw*c2) is off
+  // by a meaningful amount (|mref| >= kFastLimit: raw_mode), the scores are
+  // first shifted by r_raw in raw units, where the difference is exact for
+  // scores near the max, and the same FMA then scales them.  A row's
+  // exponents can only be large when its reference is, so the mode changes
+  // only when a reference does.
+  float mref[QB], m_use[QB], mlazy[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mref[qb] = mlazy[qb] = -INFINITY, m_use[qb] = 0.f;
+  bool raw_mode = false, d_rescale = false;
+  // Decision for the pending tile, taken as soon as its max is known.
+  auto decide = [&]() __attribute__((always_inline)) {
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) need = need || (mx[qb] * c2 > mlazy[qb]);
+    d_rescale = wave_any(need);
+  };
+
+  // One position i of the tile sequence (key tile kt, its successors kt1
+  // and kt2 at positions i+1 and i+2), software-pipelined so that every
+  // matrix instruction has vector work beside it: on entry s holds the
+  // masked raw scores of tile kt and mx their row max (both produced by the
+  // previous step).  While the exponentials of tile kt run, the score MFMAs
+  // of tile kt1 (its K is already in LDS) are issued into s_nxt; while the
+  // P V MFMAs of tile kt run, the probabilities are packed just ahead of the
+  // MFMA that consumes them and the row max of tile kt1 is taken.  K
+  // therefore streams one tile ahead of V: the copies started here are K of
+  // tile kt2 (into the buffer that held K of tile kt) and V of tile kt1.
+  // wlo1/whi1: visibility word of tile kt1 (mask mode).
+  auto step = [&](int i, int kt, int kt1, int kt2, uint32_t wlo1, uint32_t whi1, const u32x4* __restrict__ Knext,
+                  const u32x4* __restrict__ Vcur, u32x4* kdst, u32x4* vdst, f32x16 (&s)[QB][2],
+                  f32x16 (&s_nxt)[QB][2]) {
+    wait_vmem();      // K of tile kt1 and V of tile kt have landed (this wave's part)
+    __syncthreads();  // ... everyone's part; everyone is done with the previous tile
+    if (i + 2 < i_end) load_k(kt2, kdst);
+    if (i + 1 < i_end) load_v(kt1, vdst);
+
+    const int k0 = kt * BN;
+    if (!active || (CAUSAL && k0 > q0w + WQ - 1)) return;  // nothing visible
+
+    // Raise the reference when decide asked for it (rare).
+    if (d_rescale) {
+      float r_new[QB];
+      bool big = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float r_new = fmaxf(r_raw[qb], mx[qb]);
-        const float lg = exact ? (r_raw[qb] - r_new) * c2 : mref[qb] - r_new * c2;
+        r_new[qb] = fmaxf(r_raw[qb], mx[qb]);
+        const float nm = r_new[qb] * c2;
+        big = big || (fabsf(nm) >= kFastLimit && nm != -INFINITY);
+      }
+      const bool raw_new = wave_any(big);
+      const bool raw_diff = raw_mode || raw_new;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float lg = raw_diff ? (r_raw[qb] - r_new[qb]) * c2 : mref[qb] - r_new[qb] * c2;
         const float alpha = (r_raw[qb] == -INFINITY) ? 0.f : fast_exp2(lg);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) oacc[qb][i] *= alpha;
-        r_raw[qb] = r_new;
-        mref[qb] = r_new * c2;
+        r_raw[qb] = r_new[qb];
+        mref[qb] = r_new[qb] * c2;
+        mlazy[qb] = mref[qb] + kLazy;
+        m_use[qb] = (mref[qb] == -INFINITY) ? 0.f : mref[qb];
       }
+      raw_mode = raw_new;
     }
-    float m_use[QB];
+    float mu[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) m_use[qb] = (mref[qb] == -INFINITY) ? 0.f : mref[qb];
-    if (exact) {
+    for (int qb = 0; qb < QB; ++qb) mu[qb] = m_use[qb];
+    if (raw_mode) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float ru = (r_raw[qb] == -INFINITY) ? 0.f : r_raw[qb];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) s[qb][kb] -= ru;
-        m_use[qb] = 0.f;
+        mu[qb] = 0.f;
       }
     }
 
@@ -300,19 +339,17 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       constexpr int PK = 3;             // K fragments in flight
       constexpr int EPI = 32 / NS;      // exponentials per slice and query block
       const char* __restrict__ Kb = (const char*)Knext;
-      uint32_t kbase = k_off;
-      asm volatile("" : "+v"(kbase));
       u32x4 kq[PK + 1];
 #pragma unroll
       for (int i = 0; i < PK; ++i)
-        kq[i] = *(const u32x4*)(Kb + (kbase ^ (32 * (i >> 1))) + (i & 1) * 32 * RC * 16);
+        kq[i] = *(const u32x4*)(Kb + k_addr[i >> 1] + (i & 1) * 32 * RC * 16);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s_nxt[qb][0] = s_nxt[qb][1] = f32x16{};
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         if (i + PK < NS) {
           const int j = i + PK;
-          kq[j % (PK + 1)] = *(const u32x4*)(Kb + (kbase ^ (32 * (j >> 1))) + (j & 1) * 32 * RC * 16);
+          kq[j % (PK + 1)] = *(const u32x4*)(Kb + k_addr[j >> 1] + (j & 1) * 32 * RC * 16);
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -322,84 +359,134 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
 #pragma unroll
           for (int e = 0; e < EPI; ++e) {
             const int idx = i * EPI + e;
-            s[qb][idx >> 4][idx & 15] = fast_exp2(__builtin_fmaf(s[qb][idx >> 4][idx & 15], c2, -m_use[qb]));
+            s[qb][idx >> 4][idx & 15] = fast_exp2(__builtin_fmaf(s[qb][idx >> 4][idx & 15], c2, -mu[qb]));
           }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // V^T fragments of O^T += V^T P^T run PV reads ahead of their MFMAs;
-    // the first ones are issued before P is packed.
+    // O^T += V^T P^T, 16 keys per MFMA: MFMA i uses keys 16t .. 16t+15 with
+    // t = i / (D/32), which are accumulator registers 8*(t%2) .. +7 of block
+    // t/2 (see acc_row).  V^T fragments run PV reads ahead of their MFMAs.
+    // P = exp2(s*c2 - m) is packed to fp16/bf16 (round to nearest even) one
+    // dword per slice, ahead of the MFMA that reads it; for fp16 the row sum
+    // l adds the same rounded probabilities that weight V, pairwise in FP32
+    // (v_dot2 with ones); bf16 keeps only 8 bits, so there l sums the FP32
+    // values.  The slices also fold the next tile's raw scores into its row
+    // max.
     constexpr int NV = (BN / 16) * (D / 32);  // P V MFMAs per tile
     constexpr int PV = 2;
+    constexpr int NPK = NV - D / 32;          // slices that pack operands 1 .. BN/16-1
+    constexpr int WPK = (4 * (BN / 16 - 1)) / NPK;  // dwords packed per such slice
+    constexpr int MPS = 32 / NV;              // next-tile scores folded per slice
+    static_assert(WPK * NPK == 4 * (BN / 16 - 1) && MPS * NV == 32, "slice split");
     const char* __restrict__ Vl = (const char*)Vcur;
-    uint32_t vb0 = v_off0, vb1 = v_off1;
-    asm volatile("" : "+v"(vb0), "+v"(vb1));
-    auto vread = [&](int i) {
-      const int t = i / (D / 32), db = i % (D / 32);
-      const u32x2 lo = lds_read_tr16(Vl + (vb0 ^ (64 * db)) + t * 16 * RC * 16);
-      const u32x2 hi = lds_read_tr16(Vl + (vb1 ^ (64 * db)) + t * 16 * RC * 16);
-      return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
-    u32x4 vq[PV + 1];
+    auto pv_phase = [&]() __attribute__((always_inline)) {
+      auto vread = [&](int i) {
+        const int t = i / (D / 32), db = i % (D / 32);
+        const u32x2 lo = lds_read_tr16(Vl + v_addr[0][db] + t * 16 * RC * 16);
+        const u32x2 hi = lds_read_tr16(Vl + v_addr[1][db] + t * 16 * RC * 16);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      u32x4 vq[PV + 1];
 #pragma unroll
-    for (int i = 0; i < PV; ++i) vq[i] = vread(i);
+      for (int i = 0; i < PV; ++i) vq[i] = vread(i);
 
-    // P = exp2(s*c2 - m) (computed above), packed to fp16/bf16 (round to
-    // nearest even) as the B operand of O^T += V^T P^T.  For fp16 the row
-    // sum l adds the same rounded probabilities that weight V, pairwise in
-    // FP32 (v_dot2 with ones); bf16 keeps only 8 bits, so there l sums the
-    // FP32 values.
-    u32x4 pf[QB][BN / 16];
+      u32x4 pf[QB][BN / 16];
+      float lsum[QB], mn[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
+        lsum[qb] = 0.f;
+        mn[qb] = -INFINITY;
+      }
+      // dword idx (0 .. 4*BN/16-1) of the packed operands: operand idx/4,
+      // elements 2*(idx%4), +1 of its eight.
+      auto pack_dw = [&](int idx) __attribute__((always_inline)) {
+        const int t = idx >> 2, lo = (t & 1) * 8 + 2 * (idx & 3);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float x0 = s[qb][t >> 1][lo], x1 = s[qb][t >> 1][lo + 1];
+          pf[qb][t][idx & 3] = pack2<T>(x0, x1);
+          if constexpr (T::id == Fp16::id) {
+            lsum[qb] = add_pair<T>(pf[qb][t][idx & 3], lsum[qb]);
+          } else {
+            lsum[qb] += x0;
+            lsum[qb] += x1;
+          }
+          asm volatile("" : "+v"(lsum[qb]));  // the sum stays in this slice
+        }
+      };
       if constexpr (DROP) {
         // l sums the undropped FP32 probabilities; then the dropped ones are
         // zeroed before packing (the keep scale is applied to O at the end).
-        float lsum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) lsum += s[qb][kb][r];
-        l_run[qb] += lsum;
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint32_t keep = dropout_bits_st(k0 + kb * 32, q0w + 32 * qb + ql, (uint64_t)bh, a.drop.seed,
-                                                a.drop.offset, a.drop.thr, g);
+            for (int r = 0; r < 16; ++r) lsum[qb] += s[qb][kb][r];
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!((keep >> r) & 1u)) s[qb][kb][r] = 0.f;
+          for (int kb = 0; kb < 2; ++kb) {
+            const uint32_t keep = dropout_bits_st(k0 + kb * 32, q0w + 32 * qb + ql, (uint64_t)bh, a.drop.seed,
+                                                  a.drop.offset, a.drop.thr, g);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!((keep >> r) & 1u)) s[qb][kb][r] = 0.f;
+          }
+#pragma unroll
+          for (int t = 0; t < BN / 16; ++t) pf[qb][t] = pack8<T>(s[qb][t >> 1], (t & 1) * 8);
         }
+      } else {
 #pragma unroll
-        for (int t = 0; t < BN / 16; ++t) pf[qb][t] = pack8<T>(s[qb][t >> 1], (t & 1) * 8);
-        continue;
+        for (int e = 0; e < 4; ++e) pack_dw(e);
       }
-      float lsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < BN / 16; ++t) {
-        pf[qb][t] = pack8<T>(s[qb][t >> 1], (t & 1) * 8);
-        if constexpr (T::id == Fp16::id) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lsum = add_pair<T>(pf[qb][t][e], lsum);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) lsum += s[qb][t >> 1][(t & 1) * 8 + e];
-        }
-      }
-      l_run[qb] += lsum;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // O^T += V^T P^T, 16 keys per step: step t uses keys 16t .. 16t+15, which
-    // are accumulator registers 8*(t%2) .. +7 of block t/2 (see acc_row).
-    // Each V^T fragment feeds the QB query blocks.
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      if (i + PV < NV) vq[(i + PV) % (PV + 1)] = vread(i + PV);
-      const int t = i / (D / 32), db = i % (D / 32);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<T>(vq[i % (PV + 1)], pf[qb][t], oacc[qb][db]);
       __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (i + PV < NV) vq[(i + PV) % (PV + 1)] = vread(i + PV);
+        const int t = i / (D / 32), db = i % (D / 32);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<T>(vq[i % (PV + 1)], pf[qb][t], oacc[qb][db]);
+        if constexpr (!DROP) {
+          if (i < NPK) {
+#pragma unroll
+            for (int w = 0; w < WPK; ++w) pack_dw(4 + i * WPK + w);
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int e = 0; e < MPS; ++e) {
+            const int idx = i * MPS + e;
+            mn[qb] = fmaxf(mn[qb], s_nxt[qb][idx >> 4][idx & 15]);
+          }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(mn[qb]));  // the max stays in this slice
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        l_run[qb] += lsum[qb];
+        mx[qb] = xhalf_max(mn[qb]);
+      }
+      decide();
+    };
+
+    // The row max of tile kt1 is taken during the loop (on a last position
+    // it is that of stale scores and never used); when tile kt1 needs a mask
+    // it is masked afterwards and its max taken again.  Tile kt1 is pending
+    // for the next step unless this is the last position or the whole tile
+    // lies above this wave's queries.
+    pv_phase();
+    const int k1 = kt1 * BN;
+    const bool pending = i + 1 < i_end && !(CAUSAL && k1 > q0w + WQ - 1);
+    const bool mask1 = (CAUSAL && k1 + BN - 1 > q0w) || (MASK ? (wlo1 & whi1) != 0xffffffffu : k1 + BN > N);
+    if (pending && mask1) {
+      asm volatile("");  // keeps this a branch: the masking is not speculated
+      mask_tile(s_nxt, k1, wlo1, whi1);
+      tile_max(s_nxt);
+      decide();
     }
   };
 
@@ -413,8 +500,13 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       if (i_begin + 1 < i_end) load_k(i_begin + 1, lds_k1);
       wait_vmem();
       __syncthreads();
-      if (active) scores(lds_k0, sA);
       constexpr uint32_t kAll = 0xffffffffu;
+      if (active) {
+        scores(lds_k0, sA);
+        mask_tile(sA, i_begin * BN, kAll, kAll);
+        tile_max(sA);
+        decide();
+      }
       for (int kt = i_begin; kt < i_end; kt += 2) {
         step(kt, kt, kt + 1, kt + 2, kAll, kAll, lds_k1, lds_v0, lds_k0, lds_v1, sA, sB);
         if (kt + 1 < i_end) step(kt + 1, kt + 1, kt + 2, kt + 3, kAll, kAll, lds_k0, lds_v1, lds_k1, lds_v0, sB, sA);
@@ -434,7 +526,12 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     if (i_begin + 1 < i_end) load_k(kt_n, lds_k1);
     wait_vmem();
     __syncthreads();
-    if (active) scores(lds_k0, sA);
+    if (active) {
+      scores(lds_k0, sA);
+      mask_tile(sA, kt_c * BN, w_lo, w_hi);
+      tile_max(sA);
+      decide();
+    }
     // One position: the carried tiles advance by one and position i+2 is
     // looked up first (before the step's wait, which any window refill shares).
     auto run = [&](int i, const u32x4* Kn, const u32x4* Vc, u32x4* kd, u32x4* vd, f32x16 (&s)[QB][2],
@@ -445,7 +542,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
         kt2 = win.tile(i + 2, lane);
         win.word(i + 2, lo2, hi2);
       }
-      step(i, kt_c, kt_n, kt2, w_lo, w_hi, Kn, Vc, kd, vd, s, sn);
+      step(i, kt_c, kt_n, kt2, wn_lo, wn_hi, Kn, Vc, kd, vd, s, sn);
       kt_c = kt_n;
       kt_n = kt2;
       w_lo = wn_lo;
