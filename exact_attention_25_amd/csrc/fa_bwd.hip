@@ -336,22 +336,32 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     const float ks = DROP ? a.drop.keep_scale : 1.f;
     auto softmax_elem = [&](int qb, int r) {
       const float p = fast_exp2(__builtin_fmaf(s[qb][r], c2, -lse_r[qb][r]));
+      float pv, ds;
       if constexpr (DROP) {
         const bool keep = (kbits[qb] >> r) & 1u;
-        s[qb][r] = keep ? p * ks : 0.f;                        // dropped, scaled P for dV
-        dp[qb][r] = p * ((keep ? dp[qb][r] * ks : 0.f) - dl_r[qb][r]);  // dS
+        pv = keep ? p * ks : 0.f;                                // dropped, scaled P for dV
+        ds = p * ((keep ? dp[qb][r] * ks : 0.f) - dl_r[qb][r]);  // dS
       } else {
-        s[qb][r] = p;
-        dp[qb][r] = p * (dp[qb][r] - dl_r[qb][r]);
+        pv = p;
+        ds = p * (dp[qb][r] - dl_r[qb][r]);
       }
+      // The results stay in this slice (IR-level sinking would otherwise
+      // move them past the slice's MFMA, out of its shadow).
+      asm volatile("" : "+v"(pv), "+v"(ds));
+      s[qb][r] = pv;
+      dp[qb][r] = ds;
     };
     u32x4 pf[2][2], sf[2][2];
-    auto pack_block = [&](int qb) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        pf[qb][t2] = pack8<T>(s[qb], t2 * 8);
-        sf[qb][t2] = pack8<T>(dp[qb], t2 * 8);
-      }
+    // One dword of block qb's packed operands: idx 0-3 P and 4-7 dS of
+    // queries 0-7 of each run (t2 = 0), 8-15 the same for t2 = 1.  The dV/dK
+    // MFMAs of a block use t2 = 0 first, so the t2 = 1 half is packed in the
+    // shadow of those MFMAs.
+    auto pack_dw = [&](int qb, int idx) __attribute__((always_inline)) {
+      const int t2 = idx >> 3, e = idx & 3, lo = t2 * 8 + 2 * e;
+      uint32_t w = (idx & 4) ? pack2<T>(dp[qb][lo], dp[qb][lo + 1]) : pack2<T>(s[qb][lo], s[qb][lo + 1]);
+      asm volatile("" : "+v"(w));  // packed in this slice
+      if (idx & 4) sf[qb][t2][e] = w;
+      else pf[qb][t2][e] = w;
     };
     auto mfma1 = [&](int m, u32x4 f) {  // S or dP MFMA m of the tile
       const int qb = m / N1, n = m % N1;
@@ -390,7 +400,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
         if ((m - N1) * E1 + e < 16) softmax_elem(0, (m - N1) * E1 + e);
       __builtin_amdgcn_sched_barrier(0);
     }
-    pack_block(0);
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) pack_dw(0, idx);
     mask_block(1);
     u32x4 tq[PT + 1];
 #pragma unroll
@@ -402,18 +413,21 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     for (int m = 0; m < N3; ++m) {
       tq[(m + PT) % (PT + 1)] = tr_frag(m + PT);
       mfma3(m, tq[m % (PT + 1)]);
+      if (m < 8) pack_dw(0, 8 + m);
 #pragma unroll
       for (int e = 0; e < E3; ++e)
         if (m * E3 + e < 16) softmax_elem(1, m * E3 + e);
       __builtin_amdgcn_sched_barrier(0);
     }
-    pack_block(1);
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) pack_dw(1, idx);
     __builtin_amdgcn_sched_barrier(0);
     // stage 4: dV, dK of block 1
 #pragma unroll
     for (int m = N3; m < 2 * N3; ++m) {
       if (m + PT < 2 * N3) tq[(m + PT) % (PT + 1)] = tr_frag(m + PT);
       mfma3(m, tq[m % (PT + 1)]);
+      if (m - N3 < 8) pack_dw(1, 8 + m - N3);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -718,8 +732,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     const float ks = DROP ? a.drop.keep_scale : 1.f;
     auto softmax_elem = [&](int kb, int r) {
       const float p = fast_exp2(__builtin_fmaf(s[kb][r], c2, -lse2));
-      if constexpr (DROP) dp[kb][r] = p * ((((keep[kb] >> r) & 1u) ? dp[kb][r] * ks : 0.f) - dl);
-      else dp[kb][r] = p * (dp[kb][r] - dl);
+      float ds;
+      if constexpr (DROP) ds = p * ((((keep[kb] >> r) & 1u) ? dp[kb][r] * ks : 0.f) - dl);
+      else ds = p * (dp[kb][r] - dl);
+      asm volatile("" : "+v"(ds));  // the result stays in this slice
+      dp[kb][r] = ds;
     };
     u32x4 sf[BN / 16];
     auto pack_block = [&](int kb) {
