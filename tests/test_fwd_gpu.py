@@ -9,7 +9,7 @@ import exact_attention_25_amd as fa
 from exact_attention_25_amd import binding, workloads
 from exact_attention_25_amd.inputs import make_inputs, round_to
 from oracle import attention_forward
-from parity import assert_fwd_close, say, to_dev, to_host
+from parity import LSE_TOL, assert_fwd_close, o_error_ok, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +92,39 @@ def test_fwd_largest_fp16_scale_one(D):
     assert np.all(on == 65504.0)
     # the score 65504^2*D is rounded to fp32 on the GPU: compare LSE relatively
     assert np.abs(ln - lse_ref).max() <= 1e-6 * np.abs(lse_ref).max()
+
+
+@pytest.mark.parametrize("kind", ["rise", "fall"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_reference_mode_transitions(kind, causal, D):
+    """Rows whose running max crosses |scale*log2e*m| = 4096 mid-sequence.
+    rise: keys 0-127 give scores of a few units, later keys about +-64*D
+    (the reference is raised into the raw-score mode); fall: keys 0-127 give
+    scores about -64*D (raw mode from the first tile), later keys a few
+    units (the reference rises back into the one-FMA mode).  Every product
+    and partial sum of the scores is a multiple of 1/512 below 2^14, so FP32
+    accumulation is exact and the probabilities can be held to the usual
+    bound even at these magnitudes."""
+    rng = np.random.default_rng(400 + D + 2 * causal + (kind == "fall"))
+    B, H, N = 1, 2, 300
+    ints = lambda lo, hi, *s: rng.integers(lo, hi, size=s).astype(np.float32)
+    q = 8.0 + ints(-2, 3, B, H, N, D) / 8
+    small = ints(-16, 17, B, H, N, D) / 64
+    sign = np.where(rng.random((B, H, N, 1)) < 0.5, -1.0, 1.0).astype(np.float32)
+    big = (8.0 + ints(-4, 5, B, H, N, D) / 8) * (sign if kind == "rise" else -1.0)
+    first = np.arange(N)[None, None, :, None] < 128
+    k = np.where(first, small if kind == "rise" else big, big if kind == "rise" else small).astype(np.float32)
+    inp = {"q": q, "k": k, "v": round_to(rng.standard_normal((B, H, N, D)).astype(np.float32), "fp16")}
+    assert np.array_equal(round_to(q, "fp16"), q) and np.array_equal(round_to(k, "fp16"), k)
+    o, lse = run_fwd(inp, "fp16", causal, 1.0)
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], causal, 1.0)
+    on, ln = to_host(o), to_host(lse)
+    assert np.all(np.isfinite(on)) and np.all(np.isfinite(ln))
+    ok, max_abs, _ = o_error_ok(on, o_ref, "fp16")
+    assert ok, "O error %.3e" % max_abs
+    # |LSE| reaches ~6e3 here: a few fp32 ulps of it on top of the usual bound
+    assert np.all(np.abs(ln - lse_ref) <= LSE_TOL + 1e-6 * np.abs(lse_ref))
 
 
 def test_fwd_plus_minus_1e4_mixture():
