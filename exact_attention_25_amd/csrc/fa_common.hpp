@@ -239,12 +239,27 @@ constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
 constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
 constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
 
+// The 128-bit product a*m as (hi, lo) from four 32x32->64 multiply-adds
+// (v_mad_u64_u32): with a = a1:a0 and m = m1:m0 in 32-bit halves,
+// t = a0*m1 + hi(a0*m0) and u = a1*m0 + lo(t) cannot overflow 64 bits, the
+// low word is lo(a0*m0) | lo(u) << 32 and the high word a1*m1 + hi(t) + hi(u).
+__device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t m, uint64_t& hi, uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
+  const uint64_t p00 = (uint64_t)a0 * m0;
+  const uint64_t t = (uint64_t)a0 * m1 + (p00 >> 32);
+  const uint64_t u = (uint64_t)a1 * m0 + (uint32_t)t;
+  lo = (uint32_t)p00 | (u << 32);
+  hi = (uint64_t)a1 * m1 + ((t >> 32) + (u >> 32));
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
                                               uint64_t k1, uint64_t (&out)[4]) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(kPhiloxM0, c0), lo0 = kPhiloxM0 * c0;
-    const uint64_t hi1 = __umul64hi(kPhiloxM1, c2), lo1 = kPhiloxM1 * c2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(c0, kPhiloxM0, hi0, lo0);
+    mulhilo64(c2, kPhiloxM1, hi1, lo1);
     c0 = hi1 ^ c1 ^ k0;
     c1 = lo1;
     c2 = hi0 ^ c3 ^ k1;
