@@ -10,10 +10,11 @@
 //    gives the right contraction.
 //  * The 16 accumulator registers of lane l hold column n = l % 32 and rows
 //    m = 8*(r/4) + 4*(l/32) + (r%4), r = 0..15.
-//  * LDS has 64 banks of 4 bytes.  Tiles are stored as 16-byte chunks with
-//    an XOR swizzle inside every 256-byte line (see swz()), so that 16 lanes
-//    reading the same chunk column of 16 different rows hit 16 different
-//    chunk positions.
+//  * LDS has 64 banks of 4 bytes; ds_read_b128 is served 16 lanes (256
+//    bytes) at a time and ds_read_b64_tr_b16 32 lanes at a time.  Tiles are
+//    stored as 16-byte chunks with an XOR swizzle inside every 256-byte line
+//    (swz() for tiles read only by rows, dual_chunk() for tiles also read
+//    transposed), so that the lanes served together hit distinct banks.
 #pragma once
 
 #include <hip/hip_runtime.h>
