@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--mode bench|copy|fwd-only|bwd-only]
                     [--splits S] [--mask lengths|random|blocks|all]
+                    [--kv-heads G] [--dropout P]
 
 Default workload: causal fp16 attention forward, B=1 H=32 N=8192 D=128 (the
 headline metric: causal forward TFLOP/s and its fraction of the dense fp16
@@ -12,8 +13,12 @@ seeded synthetic tensors already resident in HBM.  The same run also times
 the backward (fa_bwd on the same shapes) and reports it under "bwd".
 
 Prints ONE JSON line.  Timing uses torch.cuda events on the stream the
-library launches on (torch's current stream).  The cpu_baseline leg times
-the float64 CPU oracle on a bounded sample of the same workload.
+library launches on (torch's current stream); `value` is K calls between
+two events.  After that region, "timing" adds the median and p95 of single
+calls, the median of 7 group means of back-to-back calls, and for workloads
+that fit the last-level cache the median of cold calls (each after
+overwriting 512 MB).  The cpu_baseline leg times the float64 CPU oracle on a
+bounded sample of the same workload.
 
 --mode copy runs only a plain device copy of known size; it exists so that
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters can be calibrated against a
@@ -21,6 +26,7 @@ kernel whose HBM traffic is known.
 --mode fwd-only / bwd-only launch just that pass K times (for profiling).
 --splits S times fa_fwd_splitkv with S key splits instead of fa_fwd.
 --kv-heads G gives K and V only G heads (grouped-query attention).
+--dropout P times fa_fwd_dropout / fa_bwd_dropout (seed 1234, offset 0).
 --mask KIND times fa_fwd_masked / fa_bwd_masked with a seeded key-padding
 mask (lengths / random / blocks / all); TFLOP/s then count only the visible
 (query, key) pairs, and the one-off tile-table build is reported apart.
@@ -248,6 +254,47 @@ def main():
 
     ms = timed(run_fwd, args.steps, args.warmup)
     tflops = flop_fraction * w.fwd_flops() / (ms * 1e-3) / 1e12
+
+    # Per-call statistics of the same forward, after the timed region (they
+    # do not enter `value`): median and p95 of single calls, each between its
+    # own events; the median of 7 group means of back-to-back calls (the
+    # protocol for kernels of a few microseconds); and, for workloads whose
+    # compulsory bytes fit the 256 MB last-level cache, the median of single
+    # calls each preceded by overwriting a 512 MB buffer (cold caches).
+    def per_call(fn, n, flush=None):
+        ev = []
+        for _ in range(n):
+            if flush is not None:
+                flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)
+
+    def group_median(fn, groups, k):
+        means = []
+        for _ in range(groups):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(k):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            means.append(a.elapsed_time(b) / k)
+        return float(np.median(means))
+
+    calls = per_call(run_fwd, args.steps)
+    timing = {"per_call_median_ms": round(float(np.median(calls)), 4),
+              "per_call_p95_ms": round(float(np.percentile(calls, 95)), 4),
+              "groups_median_ms": round(group_median(run_fwd, 7, max(1, args.steps // 7)), 4)}
+    if w.io_bytes_fwd() < 256e6:
+        flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        cold = per_call(run_fwd, min(args.steps, 20), flush=flush_buf.zero_)
+        timing["cold_median_ms"] = round(float(np.median(cold)), 4)
+        del flush_buf
     bwd_ms = timed(run_bwd, max(1, args.steps // 2), max(1, args.warmup // 2))
     bwd_tflops = flop_fraction * w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
 
@@ -288,6 +335,7 @@ def main():
             "traffic": traffic,
         },
         "hbm_compulsory_gbs": round(w.io_bytes_fwd() / (ms * 1e-3) / 1e9, 1),
+        "timing": timing,
         "bwd": {
             "ms_per_call": round(bwd_ms, 4),
             "tflops": round(bwd_tflops, 2),
