@@ -103,9 +103,12 @@ def cpu_baseline(w, seconds):
     import numpy as np
     from exact_attention_25_amd.inputs import make_inputs
     from oracle import attention_forward
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in pools] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in pools})) or "none"
     except Exception:
         threads = len(os.sched_getaffinity(0))
     heads_done, t_total = 0, 0.0
@@ -125,7 +128,8 @@ def cpu_baseline(w, seconds):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "%d of %d heads of %s, float64 numpy, %.1f s" % (heads_done, len(order), w.name, t_total),
+        "sample": "%d of %d heads of %s, float64 numpy (BLAS %s, %d host CPUs available), %.1f s" % (
+            heads_done, len(order), w.name, blas, len(os.sched_getaffinity(0)), t_total),
     }
 
 
