@@ -328,6 +328,12 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       }
     }
 
+    // Wave priority: the two waves sharing a SIMD are usually in different
+    // phases; the one in its P V phase (one MFMA and few vector
+    // instructions per slice) issues first, so its MFMAs keep the matrix
+    // core fed while the other wave's exponentials fill the vector port
+    // (measured +1 %).
+    __builtin_amdgcn_s_setprio(0);
     // Scores of the next tile (its K is resident), software-pipelined with
     // the exponentials of this tile: slice i issues the K read for score
     // MFMA i + PK, score MFMA i, and 32/NS of the exponentials; a scheduling
@@ -478,6 +484,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     // it is masked afterwards and its max taken again.  Tile kt1 is pending
     // for the next step unless this is the last position or the whole tile
     // lies above this wave's queries.
+    __builtin_amdgcn_s_setprio(1);
     pv_phase();
     const int k1 = kt1 * BN;
     const bool pending = i + 1 < i_end && !(CAUSAL && k1 > q0w + WQ - 1);
