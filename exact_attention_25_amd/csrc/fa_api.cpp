@@ -14,6 +14,9 @@ namespace {
 constexpr int64_t kMaxWorkgroups = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxN = int64_t(1) << 30;  // row indices inside a head are 32-bit in the kernels
 constexpr int kMaxSplits = 64;
+// Smallest scale: the backward keeps -LSE/scale in FP32, which must stay
+// finite for |LSE| up to ~2^40.
+constexpr float kMinScale = 0x1p-64f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -25,7 +28,7 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t D, int causal, float s
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_FP16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_UNSUPPORTED;
+  if (!(scale >= kMinScale) || !isfinite(scale)) return FA_ERR_UNSUPPORTED;
   // Grid sizes: B*H*ceil(N/64) workgroups at most; B*H must fit an int.
   if (B > kMaxWorkgroups / H) return FA_ERR_SHAPE;
   const int64_t bh = B * H;
@@ -196,7 +199,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_SHAPE:
       return "FA_ERR_SHAPE: B, H or N is not positive, H_kv does not divide H, or the problem is too large";
     case FA_ERR_UNSUPPORTED:
-      return "FA_ERR_UNSUPPORTED: need D in {64,128}, dtype fp16/bf16, causal 0/1, finite scale > 0";
+      return "FA_ERR_UNSUPPORTED: need D in {64,128}, dtype fp16/bf16, causal 0/1, finite scale >= 2^-64";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";

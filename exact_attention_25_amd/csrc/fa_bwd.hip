@@ -148,7 +148,7 @@ __device__ __forceinline__ int tr_offset(int r, int col) {
 // block of (query qb0 + lane % 32, keys k0w + 16*(lane / 32) ..) and the keep
 // bits are transposed through 128 bytes of LDS per wave.
 template <int D, bool CAUSAL, class T, bool MASK, bool DROP>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_kernel(BwdArgs a) {
   static_assert(!(MASK && DROP), "dropout runs without a mask");
   constexpr int BK = 128, BQ = kTileRows;
   constexpr int RC = D / 8, TC = BQ * RC;
@@ -224,16 +224,25 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
   const int qt_begin = CAUSAL ? (kt * BK) / BQ : 0;
   const float c2 = a.scale_log2;
 
-  // LSE (times log2 e) and Delta of the next tile travel through registers of
-  // threads 0..63 and are written to LDS at the end of a step.  Rows past the
-  // last query get an offset of +inf, hence P = 0 and dS = 0.
+  // The row terms of the next tile travel through registers of threads 0..63
+  // and are written to LDS at the end of a step: LSE * log2 e and Delta, or
+  // with PRE (D = 128 without dropout) the accumulator starts -LSE / scale
+  // and -Delta.  Rows past the last query (and rows that saw no key) get
+  // P = 0, hence dS = 0: an offset of +inf, or a start of -inf.
+  constexpr bool PRE = D == 128 && !DROP;
   float lse_n = 0.f, dl_n = 0.f;
   auto fetch_rows = [&](int j, int qt) {  // query head bhk*G + j, tile qt
     if (tid < BQ) {
       const int64_t rowbase = (int64_t)(bhk * G + j) * N;
       const int row = qt * BQ + tid;
-      lse_n = row < N ? lse_offset(a.lse[rowbase + row]) : INFINITY;
-      dl_n = row < N ? a.delta[rowbase + row] : 0.f;
+      if constexpr (PRE) {
+        const float l = row < N ? a.lse[rowbase + row] : -INFINITY;
+        lse_n = l == -INFINITY ? -INFINITY : -l / a.scale;
+        dl_n = row < N ? -a.delta[rowbase + row] : 0.f;
+      } else {
+        lse_n = row < N ? lse_offset(a.lse[rowbase + row]) : INFINITY;
+        dl_n = row < N ? a.delta[rowbase + row] : 0.f;
+      }
     }
   };
   auto put_rows = [&](float* ll, float* ld) {
@@ -243,7 +252,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
     }
   };
 
-  // One 64-query tile = two 32-query blocks, as a software pipeline of four
+  // D = 128 with dropout (one wave per SIMD): one 64-query tile = two
+  // 32-query blocks, as a software pipeline of four
   // stages whose slices pair one MFMA with one LDS read (kept PR reads
   // ahead) and a share of the vector work, closed by scheduling barriers:
   //   1. S, dP of block 0              (row reads of Q and dO)
@@ -434,7 +444,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
 
   // D = 64: the same work one 32-query block at a time, leaving the
   // schedule to the compiler -- the pipelined form needs more registers
-  // there and costs one wave per SIMD of occupancy, which measures slower.
+  // there and costs one wave per SIMD of occupancy, which measures slower;
+  // so does starting the accumulators at -LSE/scale and -Delta (as PRE does
+  // below), whose LDS reads then head the critical path of a block of only
+  // eight S and dP MFMAs.
   auto compute_blocks = [&](int j, int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
     const char* Qb = (const char*)Ql;
     const char* Gb = (const char*)Gl;
@@ -513,8 +526,103 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dkdv_kernel(BwdArgs
       }
     }
   };
+  // D = 128 without dropout (PRE): one 32-query block at a time, at two
+  // waves per SIMD.  The S and dP accumulators start at -LSE/scale and
+  // -Delta of their rows, read from LDS straight into them, so that
+  // P = exp2(S * scale * log2 e) and dS = P dP take no per-row operands and
+  // the rows' LSE and Delta hold no registers (with them the kernel needs
+  // more than 256 and runs one wave per SIMD).  LDS reads run PFR MFMAs
+  // ahead, and the second half of P and dS is packed beside the first dV/dK
+  // MFMAs.
+  constexpr int PFR = MASK ? 1 : 2, PFT = PFR;  // reads ahead (the mask's state leaves no room for 2)
+  auto compute_pre = [&](int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
+    const char* Qb = (const char*)Ql;
+    const char* Gb = (const char*)Gl;
+    const int q0 = qt * BQ;
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      const int qb0 = q0 + qb * 32;
+      if (CAUSAL && qb0 + 31 < k0w) continue;  // every query precedes every key
+      // Offsets opaque per block: the XORed offsets are formed beside their
+      // reads instead of being hoisted out of the loop into live registers.
+      uint32_t rb = roff0, tb0 = toff0, tb1 = toff1;
+      asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));
+      // Register r holds query qb*32 + acc_row(r, g): two runs of 8.
+      f32x16 s, dp;
+      const f32x4* lse4 = (const f32x4*)ll;
+      const f32x4* dl4 = (const f32x4*)ld;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v4 = 0; v4 < 2; ++v4) {
+          const int idx = (qb * 32 + h * 16 + g * 8) / 4 + v4;
+          const f32x4 x = lse4[idx], y = dl4[idx];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[h * 8 + v4 * 4 + e] = x[e];
+            dp[h * 8 + v4 * 4 + e] = y[e];
+          }
+        }
+      // S and dP: row fragment m is Q chunk m/2 (m even) or dO chunk m/2.
+      auto rowf = [&](int m) {
+        return *(const u32x4*)(((m & 1) ? Gb : Qb) + qb * 2 * ROW16 + (rb ^ (32 * (m >> 1))));
+      };
+      constexpr int NR = 2 * (D / 16);
+      u32x4 rq[PFR + 1];
+#pragma unroll
+      for (int m = 0; m < PFR; ++m) rq[m] = rowf(m);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        if (m + PFR < NR) rq[(m + PFR) % (PFR + 1)] = rowf(m + PFR);
+        if (m & 1) dp = mfma32<T>(rq[m % (PFR + 1)], vf[m >> 1], dp);
+        else s = mfma32<T>(rq[m % (PFR + 1)], kf[m >> 1], s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // P and dS in place.  Causal: both block starts are multiples of 32,
+      // so a block meets the diagonal only when qb0 == k0w, and there query
+      // acc_row(r, g) precedes key l32 exactly when l32 > acc_row(r, g): a
+      // lane mask per register, formed once, selected on that block.
+      const bool diag = CAUSAL && qb0 == k0w;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(s[r] * c2);
+        if (diag && l32 > acc_row(r, g)) p = 0.f;
+        s[r] = p;
+        dp[r] = p * dp[r];
+      }
+      // dV, dK: transposed fragment n = (t2*DB + db)*2 + w (w = 0: dO^T for
+      // dV, 1: Q^T for dK); queries 16*t2 .. 16*t2+15 of the block.
+      constexpr int DB = D / 32, NT = 4 * DB;
+      auto trf = [&](int n) {
+        const int w = n & 1, db = (n >> 1) % DB, t2 = (n >> 1) / DB;
+        const char* base = (w ? Qb : Gb) + (qb * 2 + t2) * ROW16;
+        const u32x2 lo = lds_read_tr16(base + (tb0 ^ (64 * db)));
+        const u32x2 hi = lds_read_tr16(base + (tb1 ^ (64 * db)));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      u32x4 pf[2], sf[2];
+      pf[0] = pack8<T>(s, 0);
+      sf[0] = pack8<T>(dp, 0);
+      u32x4 tq[PFT + 1];
+#pragma unroll
+      for (int n = 0; n < PFT; ++n) tq[n] = trf(n);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        if (n + PFT < NT) tq[(n + PFT) % (PFT + 1)] = trf(n + PFT);
+        const int w = n & 1, db = (n >> 1) % DB, t2 = (n >> 1) / DB;
+        if (w) dk[db] = mfma32<T>(tq[n % (PFT + 1)], sf[t2], dk[db]);
+        else dv[db] = mfma32<T>(tq[n % (PFT + 1)], pf[t2], dv[db]);
+        if (n == 0) pf[1] = pack8<T>(s, 8);  // queries 16..31, packed beside the t2 = 0 MFMAs
+        if (n == 1) sf[1] = pack8<T>(dp, 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
   auto compute = [&](int j, int qt, const u32x4* Ql, const u32x4* Gl, const float* ll, const float* ld) {
-    if constexpr (D == 128) compute_pipe(j, qt, Ql, Gl, ll, ld);
+    if constexpr (PRE) compute_pre(qt, Ql, Gl, ll, ld);
+    else if constexpr (D == 128) compute_pipe(j, qt, Ql, Gl, ll, ld);
     else compute_blocks(j, qt, Ql, Gl, ll, ld);
   };
 

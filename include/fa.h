@@ -29,7 +29,8 @@
  *     aligned.
  *   - Outputs must not alias inputs or each other.
  *   - Supported: D in {64, 128}; any 1 <= N <= 2^30; B, H >= 1;
- *     B*H*ceil(N/64) < 2^31; scale finite and > 0.  Anything else is
+ *     B*H*ceil(N/64) < 2^31; scale finite and >= 2^-64 (the backward
+ *     keeps -LSE/scale in FP32).  Anything else is
  *     rejected with an error code before any work is enqueued -- never
  *     silently computed ("CUDA FlashAttention ...", §9: unsupported shapes
  *     fall back explicitly).

@@ -69,7 +69,7 @@ def test_fwd_null(name):
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2),
     (dict(D=96), 3), (dict(D=256), 3), (dict(dtype=2), 3), (dict(causal=2), 3),
     (dict(N=(1 << 30) + 1), 2), (dict(scale=0.0), 3), (dict(scale=-1.0), 3),
-    (dict(scale=float("inf")), 3), (dict(scale=float("nan")), 3),
+    (dict(scale=float("inf")), 3), (dict(scale=float("nan")), 3), (dict(scale=2.0 ** -65), 3),
     (dict(q=P + 2), 4), (dict(o=P + 8), 4), (dict(lse=P + 4), 4),
     (dict(B=1 << 40, H=1 << 30), 2),
 ])

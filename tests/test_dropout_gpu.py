@@ -12,7 +12,7 @@ import torch
 import exact_attention_25_amd as fa
 from exact_attention_25_amd.inputs import make_inputs, round_to
 from oracle import attention_backward, attention_forward, dropout_keep
-from parity import assert_fwd_close, assert_grads_close, say, to_dev, to_host
+from parity import assert_fwd_close, assert_grads_close, rel_fro, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -82,8 +82,9 @@ def test_dropout_is_regenerated_deterministically():
     assert not torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])  # LSE is the undropped one
 
 
-def test_dropout_zero_probability_matches_plain_forward():
-    inp = make_inputs(2, 2, 300, 128, "bf16", seed=7300, with_dout=True)
+@pytest.mark.parametrize("D", [64, 128])
+def test_dropout_zero_probability_matches_plain_forward(D):
+    inp = make_inputs(2, 2, 300, D, "bf16", seed=7300, with_dout=True)
     q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
     o0, l0 = fa.fwd(q, k, v, causal=True)
     o1, l1 = fa.fwd_dropout(q, k, v, 0.0, 1, 2, causal=True)
@@ -91,8 +92,23 @@ def test_dropout_zero_probability_matches_plain_forward():
     g1 = fa.bwd_dropout(q, k, v, o1, l1, do, 0.0, 1, 2, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.allclose(l0, l1, atol=1e-6, rtol=0)
-    for a, b in zip(g0, g1):
-        assert torch.equal(a, b)
+    assert torch.equal(g0[0], g1[0])  # dQ: the same arithmetic
+    for a, b in zip(g0[1:], g1[1:]):
+        if D == 64:
+            assert torch.equal(a, b)
+        else:
+            # dK, dV at D = 128: the plain kernel starts the S and dP
+            # accumulators at -LSE/scale and -Delta, the dropout kernel
+            # subtracts them afterwards.  The FP32 values of P and dS differ
+            # by rounding order only, but that can flip their rounding to
+            # bf16 before the dV/dK products, so single elements may differ
+            # by a few units in the last place: the tensors agree to well
+            # inside the oracle tolerance.
+            r = rel_fro(to_host(a), to_host(b))
+            say("  p = 0, D = 128: plain vs dropout relative difference %.2e" % r)
+            assert r <= 2e-3
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], True, 1 / np.sqrt(D))
+    assert_grads_close([to_host(t) for t in g1], ref, "p=0 D=%d" % D)
 
 
 def test_dropout_long_sampled_heads():
