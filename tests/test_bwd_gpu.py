@@ -61,3 +61,17 @@ def test_bwd_is_bitwise_deterministic():
     b = run_fwd_bwd(inp, "fp16", True, 0.125)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("scale", [2.0 ** -64, 2.0 ** -20, 4.0])
+def test_bwd_extreme_scales(D, scale):
+    # The smallest accepted scale (2^-64: P is uniform to FP32 precision and
+    # dQ, dK are ~2^-64, still normal in bf16), a small one, and a large one
+    # (peaked rows).  At D = 128 the dK/dV kernel starts its accumulators at
+    # -LSE/scale, which is ~1e20 at the smallest scale.
+    say("bwd scale %g D=%d" % (scale, D))
+    inp = make_inputs(1, 2, 192, D, "bf16", seed=7700 + D, with_dout=True)
+    got = [to_host(t) for t in run_fwd_bwd(inp, "bf16", True, scale)]
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], True, scale)
+    assert_grads_close(got, ref, "scale %g D=%d" % (scale, D))
