@@ -164,8 +164,10 @@ def test_bwd_masked(B, H, N, D, causal, dtype, kind):
     assert np.all(got[0][empty] == 0)
 
 
-def test_bwd_masked_rows_without_keys():
-    B, H, N, D = 1, 2, 150, 64
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_masked_rows_without_keys(D):
+    # at D = 128 the dK/dV accumulators of such rows start at -inf
+    B, H, N = 1, 2, 150
     inp = make_inputs(B, H, N, D, "fp16", seed=5800, with_dout=True)
     m = make_key_mask(B, N, "random", seed=5801, p=0.05)
     m[0, :3] = 0  # causal rows 0..2 see no key
