@@ -62,6 +62,8 @@ def load_library():
     lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv_num_splits.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.fa_fwd_splitkv_num_splits.restype = ctypes.c_int
     lib.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_gqa_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
@@ -126,6 +128,11 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, num_splits
 
 def fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits):
     return int(load_library().fa_fwd_splitkv_workspace_bytes(B, H, N, D, int(causal), int(dtype), int(num_splits)))
+
+
+def splitkv_num_splits(B, H, N, D, causal):
+    """fa_fwd_splitkv_num_splits: the library's split count for a shape."""
+    return int(load_library().fa_fwd_splitkv_num_splits(B, H, N, D, int(causal)))
 
 
 def bwd_workspace_bytes(B, H, N, D, causal, dtype):
@@ -241,12 +248,15 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
     return out, lse
 
 
-def fwd_splitkv(q, k, v, num_splits, causal=False, scale=None, out=None, lse=None, workspace=None):
+def fwd_splitkv(q, k, v, num_splits=None, causal=False, scale=None, out=None, lse=None, workspace=None):
     """fa_fwd_splitkv: the forward with keys split into num_splits ranges and
-    the partial states merged.  Returns (o, lse) like fwd."""
+    the partial states merged (num_splits=None: fa_fwd_splitkv_num_splits's
+    choice for the shape).  Returns (o, lse) like fwd."""
     import torch
     B, H, N, D = q.shape
     _check({"q": q, "k": k, "v": v}, q.shape, q.dtype, q.device)
+    if num_splits is None:
+        num_splits = splitkv_num_splits(B, H, N, D, causal)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     code = _dtype_code(q)

@@ -230,6 +230,17 @@ size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D
   return align256(rows * sizeof(float)) + align256(rows * static_cast<size_t>(D) * sizeof(float));
 }
 
+int fa_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t D, int causal) {
+  if (check_common(B, H, N, D, causal, 1.0f, FA_FP16) != FA_OK) return 0;
+  // Measured on MI355X (fp16, D = 128): B1 H1 N16384 runs at 481 TFLOP/s in
+  // one pass and 939 with 4 splits; B2 H8 N2048 (256 workgroups, 1024-key
+  // ranges at S = 2) is fastest unsplit.
+  const int64_t wg = B * H * ((N + 127) / 128);
+  int s = 1;
+  while (s < 16 && wg * s < 512 && N / (2 * s) >= 2048) s *= 2;
+  return s;
+}
+
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                    int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, void* workspace,
                    size_t workspace_bytes, void* stream) {

@@ -114,6 +114,18 @@ size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D
                                       int causal, int dtype, int num_splits);
 
 /*
+ * fa_fwd_splitkv_num_splits -- a split count for fa_fwd_splitkv on this
+ * shape ("CUDA FlashAttention ...", §7: split along K when N is long and
+ * B*H is small, so that there are enough workgroups).  The forward runs one
+ * workgroup per 128 queries, W = B*H*ceil(N/128) of them; the count doubles,
+ * from 1, while W*S < 512 (two workgroups per compute unit), each of the S
+ * ranges would keep at least 2048 keys after the doubling, and S < 16.
+ * Returns 1 when splitting would not pay (for example B=1 H=32 N=8192), and
+ * 0 for a shape fa_fwd would reject.  Host-only: no GPU work.
+ */
+int fa_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t D, int causal);
+
+/*
  * fa_fwd_splitkv -- the same result as fa_fwd, with the keys split into
  * num_splits contiguous ranges of whole 64-key tiles ("CUDA FlashAttention
  * ...", §7: for long N and small B*H, split along K; every part yields a

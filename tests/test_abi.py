@@ -27,7 +27,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes",
                                     "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
                                     "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
+                                    "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
                                     "fa_status_str"]
 
 
@@ -119,6 +119,18 @@ def test_splitkv_workspace_bytes():
     assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 1) == 256 + 64 * 128 * 4
     assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 0) == 0
     assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 65) == 0
+
+
+@pytest.mark.parametrize("shape,splits", [
+    ((1, 1, 16384, 128, 0), 4), ((1, 2, 16384, 128, 0), 2), ((1, 1, 32768, 128, 1), 2),
+    ((1, 4, 8192, 128, 0), 2), ((2, 8, 2048, 128, 0), 1), ((1, 32, 8192, 128, 1), 1),
+    ((1, 1, 4096, 64, 0), 2), ((1, 1, 2 ** 20, 64, 1), 1), ((1, 1, 100, 64, 0), 1),
+    ((0, 1, 64, 64, 0), 0), ((1, 1, 64, 96, 0), 0), ((1, 1, 64, 64, 2), 0),
+])
+def test_splitkv_num_splits(shape, splits):
+    # doubling from 1 while B*H*ceil(N/128)*S < 512, N/(2S) >= 2048 and S < 16;
+    # the first six shapes are those measured (their fastest split count)
+    assert fb.splitkv_num_splits(*shape) == splits
 
 
 def test_mask_tiles_bytes():

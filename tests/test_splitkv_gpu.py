@@ -56,3 +56,19 @@ def test_splitkv_matches_single_pass_closely():
     # both are within the oracle tolerance; between themselves they differ by rounding only
     assert (o1.float() - o2.float()).abs().max().item() <= 2e-3
     assert (l1 - l2).abs().max().item() <= 1e-4
+
+
+def test_splitkv_chosen_split_count():
+    # one long head: the library's choice splits it (4 ranges of 2048 keys)
+    B, H, N, D = 1, 1, 8192, 64
+    assert fa.splitkv_num_splits(B, H, N, D, True) == 4
+    inp = make_inputs(B, H, N, D, "fp16", seed=3100)
+    q, k, v = (to_dev(inp[n], "fp16") for n in ("q", "k", "v"))
+    o, lse = fa.fwd_splitkv(q, k, v, causal=True)
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 2047, 2048, 4095, 6000, 8191])
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], True, 1 / np.sqrt(D), rows=rows)
+    assert_fwd_close(to_host(o)[:, :, rows], to_host(lse)[:, :, rows], o_ref, lse_ref, "fp16", "auto splits")
+    assert (o.float() - o1.float()).abs().max().item() <= 2e-3
+    assert (lse - l1).abs().max().item() <= 1e-4
