@@ -24,7 +24,8 @@ bounded sample of the same workload.
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters can be calibrated against a
 kernel whose HBM traffic is known.
 --mode fwd-only / bwd-only launch just that pass K times (for profiling).
---splits S times fa_fwd_splitkv with S key splits instead of fa_fwd.
+--splits S times fa_fwd_splitkv with S key splits instead of fa_fwd (S = auto:
+the count fa_fwd_splitkv_num_splits picks for the workload).
 --kv-heads G gives K and V only G heads (grouped-query attention).
 --dropout P times fa_fwd_dropout / fa_bwd_dropout (seed 1234, offset 0).
 --mask KIND times fa_fwd_masked / fa_bwd_masked with a seeded key-padding
@@ -65,8 +66,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--mode", default="bench", choices=["bench", "copy", "fwd-only", "bwd-only"])
-    p.add_argument("--splits", type=int, default=0,
-                   help="time fa_fwd_splitkv with this many key splits (split pass + merge) instead of fa_fwd")
+    p.add_argument("--splits", default="0",
+                   help="time fa_fwd_splitkv with this many key splits (split pass + merge) instead of fa_fwd; "
+                        "'auto': the count fa_fwd_splitkv_num_splits picks")
     p.add_argument("--dropout", type=float, default=0.0,
                    help="time fa_fwd_dropout / fa_bwd_dropout with this dropout probability (seed 1234, offset 0)")
     p.add_argument("--kv-heads", type=int, default=0,
@@ -167,6 +169,11 @@ def main():
         if args.workload not in named:
             sys.exit("unknown workload %s; choose from %s" % (args.workload, ", ".join(named)))
         w = named[args.workload]
+
+    if args.splits == "auto":
+        args.splits = fa.splitkv_num_splits(w.B, w.H, w.N, w.D, w.causal)
+    else:
+        args.splits = int(args.splits)
 
     tdt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
     inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys, with_dout=True)

@@ -109,16 +109,29 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
   return a;
 }
 
-// Backward workspace: Delta (FP32 [B*H*N]), then, when the dK/dV pass splits
-// grouped query heads into P > 1 parts, FP32 partial dK and dV
-// [P][B*H_kv*N][D] each; every section 256-byte aligned.
+// Backward workspace: Delta (FP32 [B*H*N]); then, when the dK/dV pass splits
+// its query positions into P > 1 parts, FP32 partial dK and dV
+// [P][B*H_kv*N][D] each; then, when the dQ pass splits its key tiles into
+// Q > 1 parts, FP32 partial dQ [Q][B*H*N][D]; every section 256-byte aligned.
+struct BwdLayout {
+  size_t delta, part_kv, part_q;  // section sizes (0 when absent)
+  size_t total() const { return delta + 2 * part_kv + part_q; }
+};
+BwdLayout bwd_layout(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D) {
+  BwdLayout l;
+  l.delta = align256(static_cast<size_t>(B * H * N) * sizeof(float));
+  const int kv_parts = fa::bwd_head_parts(B, H, H_kv, N);
+  l.part_kv = kv_parts > 1 ? align256(static_cast<size_t>(kv_parts) * static_cast<size_t>(B * H_kv * N) *
+                                      static_cast<size_t>(D) * sizeof(float))
+                           : 0;
+  const int q_parts = fa::bwd_dq_parts(B, H, N);
+  l.part_q = q_parts > 1 ? align256(static_cast<size_t>(q_parts) * static_cast<size_t>(B * H * N) *
+                                    static_cast<size_t>(D) * sizeof(float))
+                         : 0;
+  return l;
+}
 size_t bwd_workspace_layout(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D) {
-  const size_t delta_bytes = align256(static_cast<size_t>(B * H * N) * sizeof(float));
-  const int parts = fa::bwd_head_parts(B, H, H_kv, N);
-  if (parts <= 1) return delta_bytes;
-  const size_t part_bytes = align256(static_cast<size_t>(parts) * static_cast<size_t>(B * H_kv * N) *
-                                     static_cast<size_t>(D) * sizeof(float));
-  return delta_bytes + 2 * part_bytes;
+  return bwd_layout(B, H, H_kv, N, D).total();
 }
 
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -143,18 +156,15 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
   a.scale_log2 = scale * kLog2e;
   a.mask = no_mask();
   dropout_args(0.f, 0, 0, &a.drop);
-  // Grouped heads: query-head parts of the dK/dV pass and their FP32 partial
-  // sums, placed after Delta in the workspace (see bwd_workspace_layout).
+  // Parts of the dK/dV and dQ passes and their FP32 partial sums, placed
+  // after Delta in the workspace (see bwd_layout).
+  const BwdLayout l = bwd_layout(B, H, H_kv, N, D);
+  char* ws = static_cast<char*>(workspace);
   a.head_parts = fa::bwd_head_parts(B, H, H_kv, N);
-  a.part_dk = nullptr;
-  a.part_dv = nullptr;
-  if (a.head_parts > 1) {
-    const size_t delta_bytes = align256(static_cast<size_t>(B * H * N) * sizeof(float));
-    const size_t part_bytes = align256(static_cast<size_t>(a.head_parts) * static_cast<size_t>(B * H_kv * N) *
-                                       static_cast<size_t>(D) * sizeof(float));
-    a.part_dk = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes);
-    a.part_dv = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes + part_bytes);
-  }
+  a.part_dk = a.head_parts > 1 ? reinterpret_cast<float*>(ws + l.delta) : nullptr;
+  a.part_dv = a.head_parts > 1 ? reinterpret_cast<float*>(ws + l.delta + l.part_kv) : nullptr;
+  a.dq_parts = fa::bwd_dq_parts(B, H, N);
+  a.part_dq = a.dq_parts > 1 ? reinterpret_cast<float*>(ws + l.delta + 2 * l.part_kv) : nullptr;
   return a;
 }
 
@@ -298,7 +308,7 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype) {
   if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK) return 0;
-  return align256(static_cast<size_t>(B * H * N) * sizeof(float));
+  return bwd_workspace_layout(B, H, H, N, D);
 }
 
 size_t fa_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, int causal,

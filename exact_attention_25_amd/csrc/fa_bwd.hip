@@ -169,7 +169,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_ker
   const int bhk = blockIdx.x % BHkv;       // K/V head; its query heads are bhk*G .. bhk*G+G-1
   const int part = (blockIdx.x / BHkv) % n_parts;
   const int kt = blockIdx.x / (BHkv * n_parts);  // key tiles heaviest (lowest) first
-  const int j_begin = part * G / n_parts, j_end = (part + 1) * G / n_parts;  // this part's query heads
   const int64_t head = (int64_t)bhk * N * D;
 
   const int k0w = kt * BK + wave * 32;
@@ -626,13 +625,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_ker
     else compute_blocks(j, qt, Ql, Gl, ll, ld);
   };
 
-  // The workgroup walks positions p = 0 .. n_pos-1, position p being query
-  // tile qt of query head bhk*G + j (j-major: all tiles of a head, then the
-  // next head).  A step computes its tile and starts the copies of the next
-  // position's tile (jn, qtn) into the other buffers.
+  // The positions of this K/V head and key tile are the query tiles qt of
+  // query heads bhk*G + j, j-major (all tiles of a head, then the next head);
+  // this part walks its contiguous range of them, as p = 0 .. n_pos-1.  A
+  // step computes its tile and starts the copies of the next position's tile
+  // (jn, qtn) into the other buffers.
   const int qt_end = wg_any ? n_qt : qt_begin;  // workgroup-uniform
   const int nq = qt_end - qt_begin;
-  const int n_pos = (j_end - j_begin) * nq;
+  const int64_t n_all = (int64_t)G * nq;
+  const int64_t pos0 = part * n_all / n_parts;
+  const int n_pos = (int)((part + 1) * n_all / n_parts - pos0);
+  const int j_begin = nq > 0 ? (int)(pos0 / nq) : 0;
+  const int qt_first = nq > 0 ? qt_begin + (int)(pos0 % nq) : qt_begin;
   auto load = [&](int j, int qt, u32x4* Qn, u32x4* Gn) {
     const int64_t off = (int64_t)(bhk * G + j) * N * D + (int64_t)qt * BQ * D;
     const int valid = min(BQ, (int)N - qt * BQ);
@@ -659,11 +663,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_ker
   };
 
   if (n_pos > 0) {
-    load(j_begin, qt_begin, lq0, lg0);
-    fetch_rows(j_begin, qt_begin);
+    load(j_begin, qt_first, lq0, lg0);
+    fetch_rows(j_begin, qt_first);
     put_rows(ll0, ld0);
   }
-  int j_c = j_begin, qt_c = qt_begin;
+  int j_c = j_begin, qt_c = qt_first;
   for (int p = 0; p < n_pos; p += 2) {
     int j1 = j_c, qt1 = qt_c;
     advance(j1, qt1);
@@ -685,7 +689,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_ker
       dv[i] = f32x16{};
     }
   }
-  if (n_parts > 1) {  // FP32 partial sums of this part's query heads
+  if (n_parts > 1) {  // FP32 partial sums of this part's positions
     const int64_t prow = ((int64_t)part * BHkv + bhk) * N + my_k;
     float* pk = a.part_dk + prow * D;
     float* pv = a.part_dv + prow * D;
@@ -742,8 +746,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const int64_t N = a.N;
   const int n_qtiles = (int)((N + BM - 1) / BM);
   const int G = a.H / a.Hkv;  // query heads per K/V head
+  const int n_dqp = a.dq_parts;
   const int bh = head_of_slot(blockIdx.x % a.BH, a.BH, G);
-  const int rank = blockIdx.x / a.BH;
+  const int dpart = (blockIdx.x / a.BH) % n_dqp;  // this workgroup's part of the key tiles
+  const int rank = blockIdx.x / (a.BH * n_dqp);
   const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
   const int64_t head = (int64_t)bh * N * D;
   const int64_t kv_head = (int64_t)(bh / G) * N * D;
@@ -908,10 +914,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 
   constexpr uint32_t kAll = 0xffffffffu;
   if constexpr (!MASK) {
+    // this part's key tiles: kt_lo .. kt_hi-1
+    const int kt_lo = (int)((int64_t)dpart * n_kt / n_dqp), kt_hi = (int)((int64_t)(dpart + 1) * n_kt / n_dqp);
     auto step = [&](int kt, const u32x4* Kl, const u32x4* Vl, u32x4* Kn, u32x4* Vn) {
       wait_vmem();
       __syncthreads();
-      if (kt + 1 < n_kt) {
+      if (kt + 1 < kt_hi) {
         const int valid = min(BN, (int)N - (kt + 1) * BN);
         copy_tile<D>(Kh + (int64_t)(kt + 1) * BN * D, ksrc0, Kn, wave, valid);
         copy_tile<D>(Vh + (int64_t)(kt + 1) * BN * D, vsrc0, Vn, wave, valid);
@@ -919,29 +927,34 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
       if (!active || (CAUSAL && kt * BN > q0w + 31)) return;
       compute(kt, kAll, kAll, Kl, Vl);
     };
-    copy_tile<D>(Kh, ksrc0, lk0, wave, min(BN, (int)N));
-    copy_tile<D>(Vh, vsrc0, lv0, wave, min(BN, (int)N));
-    for (int kt = 0; kt < n_kt; kt += 2) {
+    if (kt_lo < kt_hi) {
+      const int valid = min(BN, (int)N - kt_lo * BN);
+      copy_tile<D>(Kh + (int64_t)kt_lo * BN * D, ksrc0, lk0, wave, valid);
+      copy_tile<D>(Vh + (int64_t)kt_lo * BN * D, vsrc0, lv0, wave, valid);
+    }
+    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
       step(kt, lk0, lv0, lk1, lv1);
-      if (kt + 1 < n_kt) step(kt + 1, lk1, lv1, lk0, lv0);
+      if (kt + 1 < kt_hi) step(kt + 1, lk1, lv1, lk0, lv0);
     }
   } else {
     // The batch element's non-empty key tiles below the causal limit, at
-    // positions 0 .. i_end-1; position i is tile kt_c with word (w_lo, w_hi),
-    // and the copies started in its step are of the tile at position i+1.
+    // positions 0 .. i_all-1, of which this part walks i_lo .. i_end-1;
+    // position i is tile kt_c with word (w_lo, w_hi), and the copies started
+    // in its step are of the tile at position i+1.
     const int64_t b = bh / a.H;
-    const int i_end = a.mask.prefix[b * (a.mask.n_tiles + 1) + n_kt];
+    const int i_all = a.mask.prefix[b * (a.mask.n_tiles + 1) + n_kt];
+    const int i_lo = (int)((int64_t)dpart * i_all / n_dqp), i_end = (int)((int64_t)(dpart + 1) * i_all / n_dqp);
     auto load = [&](int kt, u32x4* Kn, u32x4* Vn) {
       const int valid = min(BN, (int)N - kt * BN);
       copy_tile<D>(Kh + (int64_t)kt * BN * D, ksrc0, Kn, wave, valid);
       copy_tile<D>(Vh + (int64_t)kt * BN * D, vsrc0, Vn, wave, valid);
     };
-    if (i_end > 0) {  // workgroup-uniform
+    if (i_end > i_lo) {  // workgroup-uniform
       TileWindow win;
-      win.init(a.mask.list + b * a.mask.n_tiles, a.mask.words + b * a.mask.n_tiles, i_end, lane);
-      int kt_c = win.tile(0, lane);
+      win.init(a.mask.list + b * a.mask.n_tiles, a.mask.words + b * a.mask.n_tiles, i_end, lane, i_lo);
+      int kt_c = win.tile(i_lo, lane);
       uint32_t w_lo, w_hi;
-      win.word(0, w_lo, w_hi);
+      win.word(i_lo, w_lo, w_hi);
       load(kt_c, lk0, lv0);
       auto step = [&](int i, const u32x4* Kl, const u32x4* Vl, u32x4* Kn, u32x4* Vn) {
         int kt1 = 0;
@@ -958,7 +971,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
         w_lo = lo1;
         w_hi = hi1;
       };
-      for (int i = 0; i < i_end; i += 2) {
+      for (int i = i_lo; i < i_end; i += 2) {
         step(i, lk0, lv0, lk1, lv1);
         if (i + 1 < i_end) step(i + 1, lk1, lv1, lk0, lv0);
       }
@@ -966,6 +979,16 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   }
 
   if (!active || !real_q) return;
+  if (n_dqp > 1) {  // FP32 partial sum of this part's key tiles, not yet scaled
+    float* prow = a.part_dq + (((int64_t)dpart * a.BH + bh) * N + my_q) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *(f32x4*)(prow + db * 32 + rq * 8 + g * 4) =
+            f32x4{dq[db][rq * 4 + 0], dq[db][rq * 4 + 1], dq[db][rq * 4 + 2], dq[db][rq * 4 + 3]};
+    return;
+  }
   uint16_t* row = a.dq + head + (int64_t)my_q * D;
   const float sc = a.scale;
 #pragma unroll
@@ -977,7 +1000,23 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
                 pack2<T>(dq[db][rq * 4 + 2] * sc, dq[db][rq * 4 + 3] * sc)};
 }
 
-// Sum of the query-head parts' FP32 dK, dV (in part order, so the result is
+// Sum of the key-range parts' FP32 dQ (in part order, so the result is
+// reproducible), scaled and rounded to T: D/4 threads per query row.
+template <int D, class T>
+__global__ __launch_bounds__(kThreads) void dq_reduce_kernel(const float* __restrict__ part_dq,
+                                                             uint16_t* __restrict__ dq, int64_t rows, int n_parts,
+                                                             float scale) {
+  constexpr int TPR = D / 4;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row >= rows) return;
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < n_parts; ++p) s += *(const f32x4*)(part_dq + ((int64_t)p * rows + row) * D + c * 4);
+  s *= scale;
+  *(u32x2*)(dq + row * D + c * 4) = u32x2{pack2<T>(s[0], s[1]), pack2<T>(s[2], s[3])};
+}
+
+// Sum of the parts' FP32 dK, dV (in part order, so the result is
 // reproducible), dK scaled, both rounded to T: D/4 threads per key row.
 template <int D, class T>
 __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(const float* __restrict__ part_dk,
@@ -1023,8 +1062,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int64_t n_qtiles = (a.N + 127) / 128;
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, T, MASK, DROP>), dim3((unsigned)(a.BH * n_qtiles)), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, T, MASK, DROP>), dim3((unsigned)(a.BH * n_qtiles * a.dq_parts)),
+                     dim3(kThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.dq_parts <= 1) return e;
+  constexpr int rpq = kThreads / (D / 4);
+  hipLaunchKernelGGL((dq_reduce_kernel<D, T>), dim3((unsigned)((rows + rpq - 1) / rpq)), dim3(kThreads), 0, stream,
+                     a.part_dq, a.dq, rows, a.dq_parts, a.scale);
   return hipGetLastError();
 }
 

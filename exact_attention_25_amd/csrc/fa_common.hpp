@@ -190,11 +190,12 @@ struct TileWindow {
   int base;
   uint32_t t, lo, hi;
 
-  __device__ __forceinline__ void init(const int* list_b, const uint64_t* words_b, int n, int lane) {
+  // Positions start .. end-1 will be looked up.
+  __device__ __forceinline__ void init(const int* list_b, const uint64_t* words_b, int n, int lane, int start = 0) {
     list = list_b;
     words = words_b;
     end = n;
-    fill(0, lane);
+    fill(start, lane);
   }
   __device__ __forceinline__ void fill(int b0, int lane) {
     base = b0;

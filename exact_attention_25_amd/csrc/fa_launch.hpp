@@ -74,25 +74,45 @@ struct BwdArgs {
   float scale_log2;  // scale * log2(e)
   MaskTiles mask;    // key-padding mask mode only
   DropoutArgs drop;  // dropout mode only
-  // Grouped heads: the G query heads of a K/V head are split into head_parts
-  // parts; with more than one, each part writes FP32 partial dK, dV
-  // [head_parts][B*Hkv][N][D] (dK not yet scaled) and a reduce kernel sums them.
+  // Parts of the dK/dV pass: the (query head, query tile) positions a
+  // workgroup walks -- all query tiles of the G query heads that read its K/V
+  // head -- are split into head_parts contiguous ranges; with more than one,
+  // each part writes FP32 partial dK, dV [head_parts][B*Hkv][N][D] (dK not yet
+  // scaled) and a reduce kernel sums them in part order.
   int head_parts;
   float* part_dk;
   float* part_dv;
+  // Parts of the dQ pass: the key tiles a workgroup walks are split into
+  // dq_parts contiguous ranges; with more than one, each part writes FP32
+  // partial dQ [dq_parts][B*H][N][D] (not yet scaled), summed in part order.
+  int dq_parts;
+  float* part_dq;
 };
 
-// Number of query-head parts for the dK/dV pass: 1 when one workgroup per
-// (K/V head, 128 keys) already gives kWantWorkgroups, else enough parts
-// (at most G) to get there -- MQA with few K/V heads would otherwise leave
-// most of the 256 CUs idle.
+// Number of parts of the dK/dV pass: 1 when one workgroup per (K/V head,
+// 128 keys) already gives kWantWorkgroups, else enough parts to get there --
+// few K/V heads (MQA, or few heads of a long sequence) would otherwise leave
+// most of the 256 CUs idle -- but no more than one query head per part or
+// 8 query tiles (512 queries) per part on average, whichever allows more.
 constexpr int64_t kWantWorkgroups = 1024;
 inline int bwd_head_parts(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
   const int64_t G = H / Hkv;
   const int64_t wgs = B * Hkv * ((N + 127) / 128);
-  if (G <= 1 || wgs >= kWantWorkgroups) return 1;
+  if (wgs >= kWantWorkgroups) return 1;
   const int64_t parts = (kWantWorkgroups + wgs - 1) / wgs;
-  return (int)(parts < G ? parts : G);
+  const int64_t by_tiles = G * ((N + 63) / 64) / 8;
+  const int64_t cap = by_tiles > G ? by_tiles : G;
+  return (int)(parts < cap ? parts : cap);
+}
+
+// Number of key-range parts for the dQ pass (one workgroup per 128 queries):
+// the same target, at most one part per 8 key tiles (512 keys).
+inline int bwd_dq_parts(int64_t B, int64_t H, int64_t N) {
+  const int64_t wgs = B * H * ((N + 127) / 128);
+  if (wgs >= kWantWorkgroups) return 1;
+  const int64_t parts = (kWantWorkgroups + wgs - 1) / wgs;
+  const int64_t cap = ((N + 63) / 64) / 8;
+  return (int)(parts < cap ? parts : (cap > 1 ? cap : 1));
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);

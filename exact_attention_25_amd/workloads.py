@@ -6,7 +6,8 @@ storage type).  The shapes follow the pages' own measurements: causal fp16
 B=1 H=32 D=128 with N from 512 to 8192 is the benchmark of "CUDA
 FlashAttention: from online softmax to the long-sequence IO limit" (§8); the
 B=1 H=32 N=4096 D=64 shape is the validation workload of "FlashAttention
-dataflow and engineering validation on MI50" (§5.2).
+dataflow and engineering validation on MI50" (§5.2).  One head of N=16384
+is the shape the first page's split along K is for (§7: long N, small B*H).
 """
 
 from dataclasses import dataclass
@@ -62,7 +63,8 @@ LONG_BF16 = Workload("fwd_causal_b1h16n32768d128_bf16_spikyk", 1, 16, 32768, 128
                      seed=4, spiky_keys=True)
 FWDBWD_D64 = Workload("fwdbwd_causal_b1h32n4096d64_fp16", 1, 32, 4096, 64, True, "fp16", seed=5,
                       backward=True)
+FEW_HEADS_LONG = Workload("fwd_b1h1n16384d128_fp16", 1, 1, 16384, 128, False, "fp16", seed=6)
 # the workload the headline metric is quoted on
 HEADLINE = CAUSAL_D128[8192]
 
-ALL = [SMALL, NONCAUSAL_D64, *CAUSAL_D128.values(), LONG_BF16, FWDBWD_D64]
+ALL = [SMALL, NONCAUSAL_D64, *CAUSAL_D128.values(), LONG_BF16, FWDBWD_D64, FEW_HEADS_LONG]

@@ -152,7 +152,9 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 /*
  * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one FP32
  * value per query row for Delta_i = rowsum(dO_i * O_i), i.e. 4*B*H*N, rounded
- * up to 256.  Returns 0 for arguments fa_bwd would reject.
+ * up to 256; plus, when B*H*ceil(N/128) is too small to fill the GPU (few
+ * heads of a long sequence), FP32 partial dK and dV as described for
+ * fa_bwd_gqa_workspace_bytes.  Returns 0 for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
                               int causal, int dtype);
@@ -168,8 +170,10 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
  *                     ignored and on return are unspecified.
  *   other arguments : as for fa_fwd and with the same values.
  * Three kernels run in order on `stream`: Delta, then dK/dV (outer loop over
- * key tiles), then dQ (outer loop over query tiles).  No atomics are used, so
- * results are bitwise reproducible.
+ * key tiles; with few heads, split into parts over the query tiles whose
+ * FP32 partial sums a fourth kernel adds in a fixed order), then dQ (outer
+ * loop over query tiles).  No atomics are used, so results are bitwise
+ * reproducible.
  * Returns FA_OK or an fa_status error code.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -182,11 +186,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 /*
  * fa_bwd_gqa_workspace_bytes -- bytes of device workspace fa_bwd_gqa and
  * fa_bwd_masked need: Delta (4*B*H*N), plus, when the dK/dV pass splits the
- * query heads of each group into P > 1 parts (few K/V heads: the pass would
- * otherwise have too few workgroups to fill the GPU), FP32 partial dK and
- * dV of 4*P*B*H_kv*N*D bytes each; sections rounded up to 256.  Returns 0
- * for arguments fa_bwd_gqa would reject.  Equals fa_bwd_workspace_bytes
- * when H_kv = H.
+ * query positions of each K/V head (its G query heads' query tiles) into
+ * P > 1 parts (few K/V heads: the pass would otherwise have too few
+ * workgroups to fill the GPU; P is at most the larger of G and the number of
+ * 8-tile groups of query tiles), FP32 partial dK and dV of 4*P*B*H_kv*N*D bytes each; sections
+ * rounded up to 256.  Returns 0 for arguments fa_bwd_gqa would reject.
+ * Equals fa_bwd_workspace_bytes when H_kv = H.
  */
 size_t fa_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
                                   int causal, int dtype);
@@ -195,8 +200,8 @@ size_t fa_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N,
  * fa_bwd_gqa -- fa_bwd for a forward computed by fa_fwd_gqa.
  *   dk, dv : [B, H_kv, N, D]; every other tensor as in fa_fwd_gqa / fa_bwd.
  * The gradient of a shared K/V head is the sum over the H / H_kv query heads
- * that read it.  One workgroup per 128 keys walks the query tiles of its
- * part of the group's heads, accumulating in FP32 registers; with several
+ * that read it.  One workgroup per 128 keys walks its part of the query
+ * tiles of the group's heads, accumulating in FP32 registers; with several
  * parts a reduce kernel adds the parts' FP32 sums in a fixed order, so the
  * result is bitwise reproducible either way.
  * Workspace: fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, D, ...).

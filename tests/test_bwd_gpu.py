@@ -75,3 +75,23 @@ def test_bwd_extreme_scales(D, scale):
     got = [to_host(t) for t in run_fwd_bwd(inp, "bf16", True, scale)]
     ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], True, scale)
     assert_grads_close(got, ref, "scale %g D=%d" % (scale, D))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_one_head_split_into_parts(D, causal):
+    # B*H*ceil(N/128) = 12 workgroups: the dK/dV pass splits each key tile's
+    # 24 query tiles into 3 parts (8 each, the last tile ragged), the dQ pass
+    # each query tile's key tiles into 3 parts, and both add their FP32
+    # partial sums in part order
+    B, H, N = 1, 1, 1500
+    assert fa.bwd_workspace_bytes(B, H, N, D, causal, 0) == 6144 + 2 * 3 * N * D * 4 + 3 * N * D * 4
+    say("bwd one head in parts N=%d D=%d causal=%d" % (N, D, causal))
+    inp = make_inputs(B, H, N, D, "fp16", seed=7800 + D + causal, with_dout=True)
+    scale = 1.0 / np.sqrt(D)
+    a = run_fwd_bwd(inp, "fp16", causal, scale)
+    b = run_fwd_bwd(inp, "fp16", causal, scale)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
+    assert_grads_close([to_host(t) for t in a], ref, "one head N=%d D=%d" % (N, D))

@@ -130,3 +130,17 @@ def test_dropout_long_sampled_heads():
         assert_fwd_close(to_host(o[sl]), to_host(lse[sl]), o_ref, lse_ref, "fp16", "head %d" % h)
         grads = attention_backward(*sub, True, 0.125, dropout=drop)
         assert_grads_close([to_host(t[sl]) for t in (dq, dk, dv)], grads, "head %d" % h)
+
+
+def test_dropout_bwd_one_head_in_parts():
+    # one head of 1500 keys: both backward passes split into 3 parts
+    B, H, N, D = 1, 1, 1500, 128
+    inp = make_inputs(B, H, N, D, "fp16", seed=7400, with_dout=True)
+    q, k, v, do = (to_dev(inp[n], "fp16") for n in ("q", "k", "v", "do"))
+    p, seed, offset = 0.2, 99, 5
+    o, lse = fa.fwd_dropout(q, k, v, p, seed, offset, causal=True)
+    dq, dk, dv = fa.bwd_dropout(q, k, v, o, lse, do, p, seed, offset, causal=True)
+    torch.cuda.synchronize()
+    drop = (p, seed, offset)
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], True, 1 / np.sqrt(D), dropout=drop)
+    assert_grads_close([to_host(t) for t in (dq, dk, dv)], ref, "one head dropout")

@@ -179,3 +179,21 @@ def test_bwd_masked_rows_without_keys(D):
     assert torch.isneginf(lse[0, :, :3]).all() and (dq[0, :, :3] == 0).all()
     ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], True, 0.125, key_mask=m)
     assert_grads_close([to_host(t) for t in (dq, dk, dv)], ref, "sparse causal")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["blocks", "random"])
+def test_bwd_masked_one_head_in_parts(kind, causal, D):
+    # one head of 1500 keys: both backward passes split into 3 parts; with
+    # tile-structured masks the dQ parts divide the list of non-empty tiles
+    B, H, N = 1, 1, 1500
+    inp = make_inputs(B, H, N, D, "bf16", seed=5900 + D + causal, with_dout=True)
+    m = make_key_mask(B, N, kind, seed=5901 + causal, p=0.5)
+    q, k, v, do = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    tiles = fa.mask_tiles(torch.from_numpy(m).cuda())
+    o, lse = fa.fwd_masked(q, k, v, tiles, causal=causal, scale=0.1)
+    dq, dk, dv = fa.bwd_masked(q, k, v, o, lse, do, tiles, causal=causal, scale=0.1)
+    torch.cuda.synchronize()
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, 0.1, key_mask=m)
+    assert_grads_close([to_host(t) for t in (dq, dk, dv)], ref, "one head masked %s" % kind)
