@@ -27,7 +27,8 @@ kernel whose HBM traffic is known.
 --splits S times fa_fwd_splitkv with S key splits instead of fa_fwd (S = auto:
 the count fa_fwd_splitkv_num_splits picks for the workload).
 --kv-heads G gives K and V only G heads (grouped-query attention).
---dropout P times fa_fwd_dropout / fa_bwd_dropout (seed 1234, offset 0).
+--dropout P times fa_fwd_dropout / fa_bwd_dropout (seed 1234, offset 0);
+with --mask too, fa_fwd_masked_dropout / fa_bwd_masked_dropout.
 --mask KIND times fa_fwd_masked / fa_bwd_masked with a seeded key-padding
 mask (lengths / random / blocks / all); TFLOP/s then count only the visible
 (query, key) pairs, and the one-off tile-table build is reported apart.
@@ -211,11 +212,10 @@ def main():
         torch.cuda.synchronize()
         mask_ms = (time.perf_counter() - t0) / 10 * 1e3
 
-    if args.mask and args.dropout:
-        sys.exit("--mask and --dropout are separate entry points; pick one")
-    if args.dropout:
+    if args.dropout:  # with --mask as well: fa_fwd_masked_dropout
         def run_fwd():
-            fa.fwd_dropout(q, k, v, args.dropout, 1234, 0, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            fa.fwd_dropout(q, k, v, args.dropout, 1234, 0, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                           tiles=tiles)
     elif args.mask:
         def run_fwd():
             fa.fwd_masked(q, k, v, tiles, causal=w.causal, scale=w.scale, out=o, lse=lse)
@@ -236,7 +236,7 @@ def main():
     def run_bwd():
         if args.dropout:
             return fa.bwd_dropout(q, k, v, o, lse, do, args.dropout, 1234, 0, causal=w.causal, scale=w.scale,
-                                  workspace=ws)
+                                  workspace=ws, tiles=tiles)
         if args.mask:
             return fa.bwd_masked(q, k, v, o, lse, do, tiles, causal=w.causal, scale=w.scale, workspace=ws)
         return fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
@@ -311,7 +311,8 @@ def main():
 
     traffic = load_traffic(w.name) if args.splits == 0 and not args.mask and hkv == w.H and not args.dropout else None
     if args.dropout:
-        kernel = "fwd_kernel<%d,%s,dropout %g>" % (w.D, "causal" if w.causal else "full", args.dropout)
+        kernel = "fwd_kernel<%d,%s,%sdropout %g>" % (w.D, "causal" if w.causal else "full",
+                                                       "key mask," if args.mask else "", args.dropout)
     elif args.mask:
         kernel = "fwd_kernel<%d,%s,key mask>" % (w.D, "causal" if w.causal else "full")
     elif args.splits > 0:

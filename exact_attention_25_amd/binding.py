@@ -86,6 +86,13 @@ def load_library():
                                    ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float, _u64, _u64,
                                    _vp, ctypes.c_size_t, _vp]
     lib.fa_bwd_dropout.restype = ctypes.c_int
+    lib.fa_fwd_masked_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                          ctypes.c_float, ctypes.c_int, _vp, ctypes.c_float, _u64, _u64, _vp]
+    lib.fa_fwd_masked_dropout.restype = ctypes.c_int
+    lib.fa_bwd_masked_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                          _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_float,
+                                          _u64, _u64, _vp, ctypes.c_size_t, _vp]
+    lib.fa_bwd_masked_dropout.restype = ctypes.c_int
     lib.fa_dropout_mask.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_float, _u64, _u64, _vp]
     lib.fa_dropout_mask.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
@@ -153,6 +160,19 @@ def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, 
     return load_library().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
                                          float(scale), int(dtype), float(dropout_p), int(seed), int(offset),
                                          workspace, workspace_bytes, stream)
+
+
+def fa_fwd_masked_dropout(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, tiles, dropout_p, seed, offset,
+                          stream):
+    return load_library().fa_fwd_masked_dropout(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
+                                                int(dtype), tiles, float(dropout_p), int(seed), int(offset), stream)
+
+
+def fa_bwd_masked_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, tiles,
+                          dropout_p, seed, offset, workspace, workspace_bytes, stream):
+    return load_library().fa_bwd_masked_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
+                                                float(scale), int(dtype), tiles, float(dropout_p), int(seed),
+                                                int(offset), workspace, workspace_bytes, stream)
 
 
 def fa_dropout_mask(keep, B, H, N, dropout_p, seed, offset, stream):
@@ -375,9 +395,10 @@ def bwd_masked(q, k, v, o, lse, dout, tiles, causal=False, scale=None, workspace
     return dq, dk, dv
 
 
-def fwd_dropout(q, k, v, dropout_p, seed, offset=0, causal=False, scale=None, out=None, lse=None):
+def fwd_dropout(q, k, v, dropout_p, seed, offset=0, causal=False, scale=None, out=None, lse=None, tiles=None):
     """fa_fwd_dropout: forward with attention dropout regenerated from
-    (seed, offset).  k, v may have fewer heads (grouped).  Returns (o, lse)."""
+    (seed, offset).  k, v may have fewer heads (grouped).  With tiles (from
+    mask_tiles()), fa_fwd_masked_dropout.  Returns (o, lse)."""
     import torch
     hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
@@ -391,6 +412,15 @@ def fwd_dropout(q, k, v, dropout_p, seed, offset=0, causal=False, scale=None, ou
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check({"out": out}, q.shape, q.dtype, q.device)
     _check({"lse": lse}, (B, H, N), torch.float32, q.device)
+    if tiles is not None:
+        if tiles.numel() < fa_mask_tiles_bytes(B, N):
+            raise ValueError("tile table too small for B=%d N=%d" % (B, N))
+        st = fa_fwd_masked_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                   hkv, N, D, causal, scale, _dtype_code(q), tiles.data_ptr(), dropout_p, seed,
+                                   offset, _stream_handle(q.device))
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_masked_dropout")
+        return out, lse
     st = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, hkv, N, D,
                         causal, scale, _dtype_code(q), dropout_p, seed, offset, _stream_handle(q.device))
     if st != FA_OK:
@@ -398,8 +428,10 @@ def fwd_dropout(q, k, v, dropout_p, seed, offset=0, causal=False, scale=None, ou
     return out, lse
 
 
-def bwd_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, causal=False, scale=None, workspace=None):
-    """fa_bwd_dropout: gradients of fwd_dropout with the same (p, seed, offset)."""
+def bwd_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, causal=False, scale=None, workspace=None,
+                tiles=None):
+    """fa_bwd_dropout: gradients of fwd_dropout with the same (p, seed, offset)
+    (and the same tile table: fa_bwd_masked_dropout)."""
     import torch
     hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
@@ -413,6 +445,17 @@ def bwd_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, causal=False, 
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if tiles is not None:
+        if tiles.numel() < fa_mask_tiles_bytes(B, N):
+            raise ValueError("tile table too small for B=%d N=%d" % (B, N))
+        st = fa_bwd_masked_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, hkv, N, D,
+                                   causal, scale, code, tiles.data_ptr(), dropout_p, seed, offset,
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream_handle(q.device))
+        if st != FA_OK:
+            raise FaError(st, "fa_bwd_masked_dropout")
+        return dq, dk, dv
     st = fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, hkv, N, D, causal, scale, code,
                         dropout_p, seed, offset, workspace.data_ptr(), workspace.numel() * workspace.element_size(),

@@ -375,6 +375,37 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
       fa::launch_bwd_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
 }
 
+int fa_fwd_masked_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                          int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
+                          float dropout_p, uint64_t seed, uint64_t offset, void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!tiles) return FA_ERR_NULL;
+  if (!aligned16(tiles)) return FA_ERR_ALIGN;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
+  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
+  a.mask = mask_tiles_view(tiles, B, N);
+  return status_of(
+      fa::launch_fwd_masked_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_masked_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv,
+                          int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
+                          float dropout_p, uint64_t seed, uint64_t offset, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
+                           workspace_bytes);
+  if (st != FA_OK) return st;
+  if (!tiles) return FA_ERR_NULL;
+  if (!aligned16(tiles)) return FA_ERR_ALIGN;
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, scale, workspace);
+  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
+  a.mask = mask_tiles_view(tiles, B, N);
+  return status_of(
+      fa::launch_bwd_masked_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+}
+
 int fa_dropout_mask(uint8_t* keep, int64_t B, int64_t H, int64_t N, float dropout_p, uint64_t seed, uint64_t offset,
                     void* stream) {
   if (!keep) return FA_ERR_NULL;

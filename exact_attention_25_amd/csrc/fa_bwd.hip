@@ -149,7 +149,6 @@ __device__ __forceinline__ int tr_offset(int r, int col) {
 // bits are transposed through 128 bytes of LDS per wave.
 template <int D, bool CAUSAL, class T, bool MASK, bool DROP>
 __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_kernel(BwdArgs a) {
-  static_assert(!(MASK && DROP), "dropout runs without a mask");
   constexpr int BK = 128, BQ = kTileRows;
   constexpr int RC = D / 8, TC = BQ * RC;
   __shared__ u32x4 lq0[TC], lq1[TC], lg0[TC], lg1[TC];
@@ -734,7 +733,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_ker
 // S^T layout (one query per lane) as in the forward pass.
 template <int D, bool CAUSAL, class T, bool MASK, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
-  static_assert(!(MASK && DROP), "dropout runs without a mask");
   constexpr int BM = 128, BN = kTileRows;
   constexpr int RC = D / 8, TC = BN * RC;
   __shared__ u32x4 lk0[TC], lk1[TC], lv0[TC], lv1[TC];
@@ -1092,6 +1090,21 @@ hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream
 hipError_t launch_bwd_dropout(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_BWD_CASE(DD, CC, TT) \
   if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, false, true>(a, stream);
+  FA_BWD_CASE(64, false, Fp16)
+  FA_BWD_CASE(64, true, Fp16)
+  FA_BWD_CASE(128, false, Fp16)
+  FA_BWD_CASE(128, true, Fp16)
+  FA_BWD_CASE(64, false, Bf16)
+  FA_BWD_CASE(64, true, Bf16)
+  FA_BWD_CASE(128, false, Bf16)
+  FA_BWD_CASE(128, true, Bf16)
+#undef FA_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_masked_dropout(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_BWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_bwd_t<DD, CC, TT, true, true>(a, stream);
   FA_BWD_CASE(64, false, Fp16)
   FA_BWD_CASE(64, true, Fp16)
   FA_BWD_CASE(128, false, Fp16)

@@ -77,7 +77,7 @@ struct FwdShape {
 template <int D, int QB, bool CAUSAL, class T, bool SPLIT, bool MASK, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdArgs a) {
   static_assert(!(SPLIT && MASK), "split-K/V takes no mask");
-  static_assert(!(DROP && (SPLIT || MASK)), "dropout runs without split or mask");
+  static_assert(!(DROP && SPLIT), "dropout runs without split");
   constexpr int BM = FwdShape<QB>::BM, BN = kFwdBN, NT = kFwdThreads;
   constexpr int RC = D / 8;              // 16-byte chunks per row
   constexpr int TC = BN * RC;            // chunks per K or V tile
@@ -665,12 +665,12 @@ hipError_t launch_fwd_masked_t(FwdArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int QB, bool CAUSAL, class T>
+template <int D, int QB, bool CAUSAL, class T, bool MASK>
 hipError_t launch_fwd_dropout_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, false, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, false, MASK, true>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
                      stream, a);
   return hipGetLastError();
 }
@@ -740,7 +740,22 @@ hipError_t launch_fwd_masked(const FwdArgs& a, int D, bool causal, int dtype, hi
 
 hipError_t launch_fwd_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_FWD_CASE(DD, CC, TT) \
-  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_dropout_t<DD, kFwdQB, CC, TT>(a, stream);
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_dropout_t<DD, kFwdQB, CC, TT, false>(a, stream);
+  FA_FWD_CASE(64, false, Fp16)
+  FA_FWD_CASE(64, true, Fp16)
+  FA_FWD_CASE(128, false, Fp16)
+  FA_FWD_CASE(128, true, Fp16)
+  FA_FWD_CASE(64, false, Bf16)
+  FA_FWD_CASE(64, true, Bf16)
+  FA_FWD_CASE(128, false, Bf16)
+  FA_FWD_CASE(128, true, Bf16)
+#undef FA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_masked_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_FWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_dropout_t<DD, kFwdQB, CC, TT, true>(a, stream);
   FA_FWD_CASE(64, false, Fp16)
   FA_FWD_CASE(64, true, Fp16)
   FA_FWD_CASE(128, false, Fp16)

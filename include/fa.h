@@ -316,7 +316,27 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_dropout_mask -- write the keep mask the two calls above use:
+ * fa_fwd_masked_dropout, fa_bwd_masked_dropout -- the two calls above with a
+ * key-padding mask given by its tile table, as in fa_fwd_masked /
+ * fa_bwd_masked: hidden keys get P = 0 before dropout applies, the keep
+ * mask is the same (p, seed, offset) stream, and a row with no visible key
+ * gets O = 0, LSE = -inf, dQ = 0.  Errors as for the dropout calls, plus
+ * FA_ERR_NULL / FA_ERR_ALIGN for the table.
+ */
+int fa_fwd_masked_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                          int causal, float scale, int dtype, const void* tiles,
+                          float dropout_p, uint64_t seed, uint64_t offset, void* stream);
+int fa_bwd_masked_dropout(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout,
+                          void* dq, void* dk, void* dv,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                          int causal, float scale, int dtype, const void* tiles,
+                          float dropout_p, uint64_t seed, uint64_t offset,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_dropout_mask -- write the keep mask the dropout calls above use:
  * keep[b][h][i][j] = 1 (kept) or 0 (dropped), bytes, [B, H, N, N] on the
  * device (caller-owned, any alignment).  Meant for tests and inspection: it
  * is N*N bytes per head.  Errors: FA_ERR_NULL, FA_ERR_SHAPE (N > 2^24 or too

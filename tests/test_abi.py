@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes",
-                                    "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
-                                    "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_splitkv",
+                                    "fa_bwd_masked", "fa_bwd_masked_dropout", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
+                                    "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_masked_dropout", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
                                     "fa_status_str"]
 
@@ -232,3 +232,25 @@ def test_dropout_mask_rejects(kw, code):
     a = dict(keep=P, B=1, H=1, N=64, p=0.5, seed=1, offset=0)
     a.update(kw)
     assert fb.fa_dropout_mask(a["keep"], a["B"], a["H"], a["N"], a["p"], a["seed"], a["offset"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 8), 4), (dict(p=1.0), 3),
+                                     (dict(q=None), 1), (dict(Hkv=3), 2)])
+def test_fwd_masked_dropout_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=128, D=64, causal=1, scale=0.125, dtype=0, tiles=P,
+             p=0.1, seed=1, offset=0)
+    a.update(kw)
+    assert fb.fa_fwd_masked_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
+                                    a["D"], a["causal"], a["scale"], a["dtype"], a["tiles"], a["p"], a["seed"],
+                                    a["offset"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(p=-1.0), 3), (dict(ws=None), 5),
+                                     (dict(dk=None), 1)])
+def test_bwd_masked_dropout_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, Hkv=2, N=128, D=128, causal=0,
+             scale=0.1, dtype=1, tiles=P, p=0.2, seed=5, offset=3, ws=P, wsb=1 << 20)
+    a.update(kw)
+    assert fb.fa_bwd_masked_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                    a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"],
+                                    a["tiles"], a["p"], a["seed"], a["offset"], a["ws"], a["wsb"], None) == code

@@ -10,9 +10,9 @@ import pytest
 import torch
 
 import exact_attention_25_amd as fa
-from exact_attention_25_amd.inputs import make_inputs, round_to
+from exact_attention_25_amd.inputs import make_inputs, make_key_mask, round_to
 from oracle import attention_backward, attention_forward, dropout_keep
-from parity import assert_fwd_close, assert_grads_close, rel_fro, say, to_dev, to_host
+from parity import LSE_TOL, assert_fwd_close, assert_grads_close, o_error_ok, rel_fro, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +144,59 @@ def test_dropout_bwd_one_head_in_parts():
     drop = (p, seed, offset)
     ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], True, 1 / np.sqrt(D), dropout=drop)
     assert_grads_close([to_host(t) for t in (dq, dk, dv)], ref, "one head dropout")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["lengths", "blocks", "random"])
+def test_dropout_with_key_mask(kind, D, causal, dtype):
+    # dropout and a key-padding mask together (fa_fwd_masked_dropout,
+    # fa_bwd_masked_dropout) against the oracle with both applied; the random
+    # mask hides keys 0..2 so that causal rows 0..2 see no key at all
+    B, H, N = 2, 2, 333
+    say("dropout + %s mask D=%d causal=%d %s" % (kind, D, causal, dtype))
+    inp = make_inputs(B, H, N, D, dtype, seed=7500 + D + causal, with_dout=True)
+    m = make_key_mask(B, N, kind, seed=7501, p=0.5)
+    if kind == "random":
+        m[:, :3] = 0
+    q, k, v, do = (to_dev(inp[n], dtype) for n in ("q", "k", "v", "do"))
+    tiles = fa.mask_tiles(torch.from_numpy(m).cuda())
+    p, seed, offset = 0.25, 31337, 7
+    o, lse = fa.fwd_dropout(q, k, v, p, seed, offset, causal=causal, scale=0.1, tiles=tiles)
+    dq, dk, dv = fa.bwd_dropout(q, k, v, o, lse, do, p, seed, offset, causal=causal, scale=0.1, tiles=tiles)
+    torch.cuda.synchronize()
+    drop = (p, seed, offset)
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], causal, 0.1, key_mask=m, dropout=drop)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(to_host(lse)), empty)
+    full = ~empty
+    assert np.all(to_host(o)[empty] == 0)
+    assert o_error_ok(to_host(o)[full], o_ref[full], dtype)[0]
+    assert np.abs(to_host(lse)[full] - lse_ref[full]).max() <= LSE_TOL
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, 0.1, key_mask=m, dropout=drop)
+    assert_grads_close([to_host(t) for t in (dq, dk, dv)], ref, "dropout + %s mask" % kind)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_masked_dropout_zero_probability_is_masked_forward(dtype):
+    # bf16: the dropout path and the plain path both sum the row's FP32
+    # probabilities, so p = 0 is bitwise the masked forward.  fp16: the plain
+    # path sums the probabilities as packed to fp16 (the operand of P V), the
+    # dropout path the FP32 ones before dropping, so the results differ by
+    # that rounding only.
+    B, H, N, D = 1, 2, 400, 128
+    inp = make_inputs(B, H, N, D, dtype, seed=7600)
+    m = make_key_mask(B, N, "blocks", seed=7601, p=0.5)
+    q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
+    tiles = fa.mask_tiles(torch.from_numpy(m).cuda())
+    o0, l0 = fa.fwd_masked(q, k, v, tiles, causal=True)
+    o1, l1 = fa.fwd_dropout(q, k, v, 0.0, 3, 4, causal=True, tiles=tiles)
+    torch.cuda.synchronize()
+    if dtype == "bf16":
+        assert torch.equal(o0, o1) and torch.allclose(l0, l1, atol=1e-6, rtol=0)
+    else:
+        assert (o0.float() - o1.float()).abs().max().item() <= 1e-3
+        assert torch.equal(torch.isneginf(l0), torch.isneginf(l1))
+        fin = torch.isfinite(l0)
+        assert (l0[fin] - l1[fin]).abs().max().item() <= 1e-3
