@@ -14,9 +14,11 @@
 //  2. dkdv_kernel: one workgroup per 128 keys (32 per wave), K and V resident
 //     in VGPRs, looping over query tiles of 64 -- the outer-K/V, inner-Q order
 //     of "FlashAttention algorithm details", §4.3.2.  dK and dV accumulate in
-//     registers and are written once.
+//     registers and are written once (or, when the pass runs in parts, as
+//     FP32 partial sums that dkdv_reduce_kernel adds in part order).
 //  3. dq_kernel: one workgroup per 128 queries, Q and dO resident, looping
-//     over key tiles of 64; dQ accumulates in registers and is written once.
+//     over key tiles of 64; dQ accumulates in registers and is written once
+//     (in parts: FP32 partial sums, added by dq_reduce_kernel).
 // The streamed tiles go HBM -> LDS directly into a double-buffered ring (one
 // barrier per tile) and stay row-major; the transposed operands (Q^T, dO^T,
 // K^T) come from ds_read_b64_tr_b16, so nothing is transposed in memory.
