@@ -375,6 +375,26 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
       fa::launch_bwd_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
 }
 
+int fa_fwd_splitkv_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                           int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, float dropout_p,
+                           uint64_t seed, uint64_t offset, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
+  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H, N, scale);
+  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
+  a.n_splits = num_splits;
+  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
+  a.part_lse = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
+  return status_of(
+      fa::launch_fwd_splitkv_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+}
+
 int fa_fwd_masked_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                           int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
                           float dropout_p, uint64_t seed, uint64_t offset, void* stream) {

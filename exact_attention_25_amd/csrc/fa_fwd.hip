@@ -73,11 +73,11 @@ struct FwdShape {
 // DROP: attention dropout ([FA-WHY]-style regeneration from a Philox seed
 // and offset, see dropout_bits_st): dropped probabilities are zeroed before
 // P weights V, the row sum l keeps the undropped ones (LSE is that of the
-// undropped softmax), and O is multiplied by the keep scale at the end.
+// undropped softmax), and O is multiplied by the keep scale at the end (with
+// SPLIT, each split's O; the merge weights are those of the undropped LSEs).
 template <int D, int QB, bool CAUSAL, class T, bool SPLIT, bool MASK, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdArgs a) {
   static_assert(!(SPLIT && MASK), "split-K/V takes no mask");
-  static_assert(!(DROP && SPLIT), "dropout runs without split");
   constexpr int BM = FwdShape<QB>::BM, BN = kFwdBN, NT = kFwdThreads;
   constexpr int RC = D / 8;              // 16-byte chunks per row
   constexpr int TC = BN * RC;            // chunks per K or V tile
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     for (int qb = 0; qb < QB; ++qb) {
       const int my_q = q0w + 32 * qb + ql;
       const float l_tot = xhalf_sum(l_run[qb]);
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (DROP ? a.drop.keep_scale : 1.f);
       if (my_q >= N) continue;
       const int64_t row = (int64_t)bh * N + my_q;
       float* Orow = a.part_o + ((int64_t)split * rows + row) * D;
@@ -690,12 +690,12 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(uint8_t* __restrict__
   }
 }
 
-template <int D, int QB, bool CAUSAL, class T>
+template <int D, int QB, bool CAUSAL, class T, bool DROP>
 hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles * a.n_splits;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true, false, false>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true, false, DROP>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -777,7 +777,22 @@ hipError_t launch_dropout_mask(uint8_t* keep, int64_t BH, int64_t N, const Dropo
 
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_FWD_CASE(DD, CC, TT) \
-  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT>(a, stream);
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT, false>(a, stream);
+  FA_FWD_CASE(64, false, Fp16)
+  FA_FWD_CASE(64, true, Fp16)
+  FA_FWD_CASE(128, false, Fp16)
+  FA_FWD_CASE(128, true, Fp16)
+  FA_FWD_CASE(64, false, Bf16)
+  FA_FWD_CASE(64, true, Bf16)
+  FA_FWD_CASE(128, false, Bf16)
+  FA_FWD_CASE(128, true, Bf16)
+#undef FA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_splitkv_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_FWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT, true>(a, stream);
   FA_FWD_CASE(64, false, Fp16)
   FA_FWD_CASE(64, true, Fp16)
   FA_FWD_CASE(128, false, Fp16)

@@ -336,6 +336,20 @@ int fa_bwd_masked_dropout(const void* q, const void* k, const void* v, const voi
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_splitkv_dropout -- fa_fwd_dropout computed as fa_fwd_splitkv does
+ * (keys split into num_splits ranges, FP32 partial states, merge): each
+ * split drops and scales its probabilities, its partial LSE is that of the
+ * undropped ones, so the merge weights are unchanged.  The backward is
+ * fa_bwd_dropout.  Arguments, workspace and errors as for fa_fwd_splitkv,
+ * plus those of the dropout parameters.
+ */
+int fa_fwd_splitkv_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t D,
+                           int causal, float scale, int dtype, int num_splits,
+                           float dropout_p, uint64_t seed, uint64_t offset,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_dropout_mask -- write the keep mask the dropout calls above use:
  * keep[b][h][i][j] = 1 (kept) or 0 (dropped), bytes, [B, H, N, N] on the
  * device (caller-owned, any alignment).  Meant for tests and inspection: it

@@ -27,7 +27,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes",
                                     "fa_bwd_masked", "fa_bwd_masked_dropout", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
                                     "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_masked_dropout", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
+                                    "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
                                     "fa_status_str"]
 
 
@@ -254,3 +254,14 @@ def test_bwd_masked_dropout_rejects(kw, code):
     assert fb.fa_bwd_masked_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
                                     a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"],
                                     a["tiles"], a["p"], a["seed"], a["offset"], a["ws"], a["wsb"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(s=0), 3), (dict(p=1.0), 3), (dict(ws=None), 5), (dict(wsb=1000), 5),
+                                     (dict(q=None), 1), (dict(o=P + 8), 4)])
+def test_splitkv_dropout_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=256, D=128, causal=1, scale=0.1, dtype=1, s=4, p=0.1, seed=1,
+             offset=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    assert fb.fa_fwd_splitkv_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"],
+                                     a["causal"], a["scale"], a["dtype"], a["s"], a["p"], a["seed"], a["offset"],
+                                     a["ws"], a["wsb"], None) == code

@@ -72,3 +72,23 @@ def test_splitkv_chosen_split_count():
     assert_fwd_close(to_host(o)[:, :, rows], to_host(lse)[:, :, rows], o_ref, lse_ref, "fp16", "auto splits")
     assert (o.float() - o1.float()).abs().max().item() <= 2e-3
     assert (lse - l1).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [2, 5])
+def test_splitkv_with_dropout(splits, causal, D):
+    # each split drops and scales its probabilities; the partial LSEs are
+    # those of the undropped ones, so the merged result is the dropout
+    # forward's: checked against the oracle and against fwd_dropout
+    B, H, N = 1, 2, 700
+    inp = make_inputs(B, H, N, D, "bf16", seed=3200 + D + causal + splits)
+    q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    drop = (0.2, 4321, 9)
+    o, lse = fa.fwd_splitkv(q, k, v, splits, causal=causal, dropout=drop)
+    o1, l1 = fa.fwd_dropout(q, k, v, *drop, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], causal, 1 / np.sqrt(D), dropout=drop)
+    assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "split dropout")
+    assert (o.float() - o1.float()).abs().max().item() <= 2e-2
+    assert (lse - l1).abs().max().item() <= 1e-4
