@@ -86,9 +86,12 @@ def load_library():
                                    ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float, _u64, _u64,
                                    _vp, ctypes.c_size_t, _vp]
     lib.fa_bwd_dropout.restype = ctypes.c_int
-    lib.fa_fwd_splitkv_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
+    lib.fa_fwd_splitkv_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, _u64, _u64,
                                            _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_splitkv_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_splitkv_gqa.restype = ctypes.c_int
     lib.fa_fwd_splitkv_dropout.restype = ctypes.c_int
     lib.fa_fwd_masked_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                           ctypes.c_float, ctypes.c_int, _vp, ctypes.c_float, _u64, _u64, _vp]
@@ -166,11 +169,17 @@ def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, 
                                          workspace, workspace_bytes, stream)
 
 
-def fa_fwd_splitkv_dropout(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, num_splits, dropout_p, seed, offset,
-                           workspace, workspace_bytes, stream):
-    return load_library().fa_fwd_splitkv_dropout(q, k, v, o, lse, B, H, N, D, int(causal), float(scale), int(dtype),
-                                                 int(num_splits), float(dropout_p), int(seed), int(offset),
-                                                 workspace, workspace_bytes, stream)
+def fa_fwd_splitkv_dropout(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, dropout_p, seed,
+                           offset, workspace, workspace_bytes, stream):
+    return load_library().fa_fwd_splitkv_dropout(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
+                                                 int(dtype), int(num_splits), float(dropout_p), int(seed),
+                                                 int(offset), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_gqa(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, workspace,
+                       workspace_bytes, stream):
+    return load_library().fa_fwd_splitkv_gqa(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
+                                             int(dtype), int(num_splits), workspace, workspace_bytes, stream)
 
 
 def fa_fwd_masked_dropout(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, tiles, dropout_p, seed, offset,
@@ -283,11 +292,14 @@ def fwd_splitkv(q, k, v, num_splits=None, causal=False, scale=None, out=None, ls
                 dropout=None):
     """fa_fwd_splitkv: the forward with keys split into num_splits ranges and
     the partial states merged (num_splits=None: fa_fwd_splitkv_num_splits's
-    choice for the shape).  dropout=(p, seed, offset): fa_fwd_splitkv_dropout,
+    choice for the shape).  k, v may have fewer heads (grouped:
+    fa_fwd_splitkv_gqa).  dropout=(p, seed, offset): fa_fwd_splitkv_dropout,
     the same result as fwd_dropout.  Returns (o, lse) like fwd."""
     import torch
+    hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
-    _check({"q": q, "k": k, "v": v}, q.shape, q.dtype, q.device)
+    _check({"q": q}, q.shape, q.dtype, q.device)
+    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
     if num_splits is None:
         num_splits = splitkv_num_splits(B, H, N, D, causal)
     if scale is None:
@@ -305,10 +317,18 @@ def fwd_splitkv(q, k, v, num_splits=None, causal=False, scale=None, out=None, ls
     if dropout is not None:
         p, seed, offset = dropout
         st = fa_fwd_splitkv_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
-                                    N, D, causal, scale, code, num_splits, p, seed, offset, workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+                                    hkv, N, D, causal, scale, code, num_splits, p, seed, offset,
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream_handle(q.device))
         if st != FA_OK:
             raise FaError(st, "fa_fwd_splitkv_dropout")
+        return out, lse
+    if hkv != H:
+        st = fa_fwd_splitkv_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, hkv,
+                                N, D, causal, scale, code, num_splits, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_splitkv_gqa")
         return out, lse
     st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D,
                         causal, scale, code, num_splits, workspace.data_ptr(),

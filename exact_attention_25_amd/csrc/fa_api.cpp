@@ -198,6 +198,30 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// The split-K/V forward for H_kv K/V heads, with dropout when drop_p >= 0.
+int splitkv_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits,
+                   float drop_p, uint64_t seed, uint64_t offset, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
+  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
+  const bool drop = drop_p >= 0.f;
+  if (drop && !dropout_args(drop_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
+  a.n_splits = num_splits;
+  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
+  a.part_lse = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(drop ? fa::launch_fwd_splitkv_dropout(a, static_cast<int>(D), causal != 0, dtype, s)
+                        : fa::launch_fwd_splitkv(a, static_cast<int>(D), causal != 0, dtype, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -254,20 +278,15 @@ int fa_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t D, int ca
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                    int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  const int st = check_fwd(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
-  if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
-  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H, N, scale);
-  a.n_splits = num_splits;
-  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
-  a.part_lse = static_cast<float*>(workspace);
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
-  return status_of(
-      fa::launch_fwd_splitkv(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+  return splitkv_common(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype, num_splits, -1.f, 0, 0, workspace,
+                        workspace_bytes, stream);
+}
+
+int fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                       int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, -1.f, 0, 0, workspace,
+                        workspace_bytes, stream);
 }
 
 // ---- key-padding masks -----------------------------------------------------
@@ -376,23 +395,12 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
 }
 
 int fa_fwd_splitkv_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                           int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, float dropout_p,
-                           uint64_t seed, uint64_t offset, void* workspace, size_t workspace_bytes, void* stream) {
-  const int st = check_fwd(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
-  if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
-  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H, N, scale);
-  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
-  a.n_splits = num_splits;
-  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
-  a.part_lse = static_cast<float*>(workspace);
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
-  return status_of(
-      fa::launch_fwd_splitkv_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+                           int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits,
+                           float dropout_p, uint64_t seed, uint64_t offset, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!(dropout_p >= 0.f)) return FA_ERR_UNSUPPORTED;  // NaN or negative; the rest as for the other dropout calls
+  return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, dropout_p, seed, offset,
+                        workspace, workspace_bytes, stream);
 }
 
 int fa_fwd_masked_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,

@@ -149,6 +149,15 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int causal, float scale, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* fa_fwd_splitkv_gqa -- fa_fwd_splitkv for k, v with H_kv K/V heads (H_kv
+ * divides H; query head h reads K/V head h / (H / H_kv), as in fa_fwd_gqa).
+ * Workspace as for fa_fwd_splitkv (it holds per-query-head states); errors
+ * as for fa_fwd_splitkv plus FA_ERR_SHAPE for an H_kv that does not divide H. */
+int fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                       int causal, float scale, int dtype, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one FP32
  * value per query row for Delta_i = rowsum(dO_i * O_i), i.e. 4*B*H*N, rounded
@@ -340,11 +349,12 @@ int fa_bwd_masked_dropout(const void* q, const void* k, const void* v, const voi
  * (keys split into num_splits ranges, FP32 partial states, merge): each
  * split drops and scales its probabilities, its partial LSE is that of the
  * undropped ones, so the merge weights are unchanged.  The backward is
- * fa_bwd_dropout.  Arguments, workspace and errors as for fa_fwd_splitkv,
- * plus those of the dropout parameters.
+ * fa_bwd_dropout.  k, v have H_kv heads as in fa_fwd_gqa.  Arguments,
+ * workspace and errors as for fa_fwd_splitkv_gqa, plus those of the dropout
+ * parameters.
  */
 int fa_fwd_splitkv_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int64_t B, int64_t H, int64_t N, int64_t D,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
                            int causal, float scale, int dtype, int num_splits,
                            float dropout_p, uint64_t seed, uint64_t offset,
                            void* workspace, size_t workspace_bytes, void* stream);

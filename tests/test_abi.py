@@ -27,7 +27,8 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes",
                                     "fa_bwd_masked", "fa_bwd_masked_dropout", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
                                     "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_masked_dropout", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
+                                    "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_num_splits",
+                                    "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
                                     "fa_status_str"]
 
 
@@ -256,12 +257,23 @@ def test_bwd_masked_dropout_rejects(kw, code):
                                     a["tiles"], a["p"], a["seed"], a["offset"], a["ws"], a["wsb"], None) == code
 
 
-@pytest.mark.parametrize("kw,code", [(dict(s=0), 3), (dict(p=1.0), 3), (dict(ws=None), 5), (dict(wsb=1000), 5),
-                                     (dict(q=None), 1), (dict(o=P + 8), 4)])
+@pytest.mark.parametrize("kw,code", [(dict(s=0), 3), (dict(p=1.0), 3), (dict(p=-0.5), 3), (dict(p=float("nan")), 3),
+                                     (dict(ws=None), 5), (dict(wsb=1000), 5), (dict(q=None), 1), (dict(o=P + 8), 4),
+                                     (dict(Hkv=3), 2)])
 def test_splitkv_dropout_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=256, D=128, causal=1, scale=0.1, dtype=1, s=4, p=0.1, seed=1,
-             offset=0, ws=P, wsb=1 << 30)
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=256, D=128, causal=1, scale=0.1, dtype=1, s=4, p=0.1,
+             seed=1, offset=0, ws=P, wsb=1 << 30)
     a.update(kw)
-    assert fb.fa_fwd_splitkv_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"],
-                                     a["causal"], a["scale"], a["dtype"], a["s"], a["p"], a["seed"], a["offset"],
-                                     a["ws"], a["wsb"], None) == code
+    assert fb.fa_fwd_splitkv_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
+                                     a["D"], a["causal"], a["scale"], a["dtype"], a["s"], a["p"], a["seed"],
+                                     a["offset"], a["ws"], a["wsb"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(Hkv=3), 2), (dict(Hkv=0), 2), (dict(s=65), 3), (dict(ws=None), 5),
+                                     (dict(k=None), 1)])
+def test_splitkv_gqa_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=256, D=64, causal=0, scale=0.1, dtype=0, s=2,
+             ws=P, wsb=1 << 30)
+    a.update(kw)
+    assert fb.fa_fwd_splitkv_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["D"],
+                                 a["causal"], a["scale"], a["dtype"], a["s"], a["ws"], a["wsb"], None) == code

@@ -7,7 +7,7 @@ import torch
 
 import exact_attention_25_amd as fa
 from exact_attention_25_amd import workloads
-from exact_attention_25_amd.inputs import make_inputs
+from exact_attention_25_amd.inputs import make_inputs, round_to
 from oracle import attention_forward
 from parity import assert_fwd_close, say, to_dev, to_host
 
@@ -92,3 +92,22 @@ def test_splitkv_with_dropout(splits, causal, D):
     assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "split dropout")
     assert (o.float() - o1.float()).abs().max().item() <= 2e-2
     assert (lse - l1).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("Hkv", [1, 2])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("with_dropout", [False, True])
+def test_splitkv_grouped_heads(with_dropout, causal, Hkv):
+    # grouped K/V heads through the split forward (fa_fwd_splitkv_gqa, and
+    # fa_fwd_splitkv_dropout with H_kv < H) against the oracle
+    B, H, N, D = 2, 4, 900, 128
+    rng = np.random.default_rng(3300 + Hkv + causal + with_dropout)
+    q = round_to(rng.standard_normal((B, H, N, D), dtype=np.float32), "fp16")
+    k = round_to(rng.standard_normal((B, Hkv, N, D), dtype=np.float32), "fp16")
+    v = round_to(rng.standard_normal((B, Hkv, N, D), dtype=np.float32), "fp16")
+    qd, kd, vd = (to_dev(x, "fp16") for x in (q, k, v))
+    drop = (0.15, 77, 3) if with_dropout else None
+    o, lse = fa.fwd_splitkv(qd, kd, vd, 3, causal=causal, dropout=drop)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_forward(q, k, v, causal, 1 / np.sqrt(D), dropout=drop)
+    assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, "fp16", "split gqa")
