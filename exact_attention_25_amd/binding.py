@@ -92,6 +92,10 @@ def load_library():
     lib.fa_fwd_splitkv_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
     lib.fa_fwd_splitkv_gqa.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                          ctypes.c_float, ctypes.c_int, _vp, ctypes.c_int, ctypes.c_float, _u64, _u64,
+                                          _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_splitkv_masked.restype = ctypes.c_int
     lib.fa_fwd_splitkv_dropout.restype = ctypes.c_int
     lib.fa_fwd_masked_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                           ctypes.c_float, ctypes.c_int, _vp, ctypes.c_float, _u64, _u64, _vp]
@@ -174,6 +178,13 @@ def fa_fwd_splitkv_dropout(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dty
     return load_library().fa_fwd_splitkv_dropout(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
                                                  int(dtype), int(num_splits), float(dropout_p), int(seed),
                                                  int(offset), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_masked(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, tiles, num_splits, dropout_p,
+                          seed, offset, workspace, workspace_bytes, stream):
+    return load_library().fa_fwd_splitkv_masked(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
+                                                int(dtype), tiles, int(num_splits), float(dropout_p), int(seed),
+                                                int(offset), workspace, workspace_bytes, stream)
 
 
 def fa_fwd_splitkv_gqa(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, workspace,
@@ -289,12 +300,13 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
 
 
 def fwd_splitkv(q, k, v, num_splits=None, causal=False, scale=None, out=None, lse=None, workspace=None,
-                dropout=None):
+                dropout=None, tiles=None):
     """fa_fwd_splitkv: the forward with keys split into num_splits ranges and
     the partial states merged (num_splits=None: fa_fwd_splitkv_num_splits's
     choice for the shape).  k, v may have fewer heads (grouped:
     fa_fwd_splitkv_gqa).  dropout=(p, seed, offset): fa_fwd_splitkv_dropout,
-    the same result as fwd_dropout.  Returns (o, lse) like fwd."""
+    the same result as fwd_dropout.  tiles (from mask_tiles()):
+    fa_fwd_splitkv_masked, with or without dropout.  Returns (o, lse) like fwd."""
     import torch
     hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
@@ -314,6 +326,17 @@ def fwd_splitkv(q, k, v, num_splits=None, causal=False, scale=None, out=None, ls
     need = fwd_splitkv_workspace_bytes(B, H, N, D, causal, code, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if tiles is not None:
+        if tiles.numel() < fa_mask_tiles_bytes(B, N):
+            raise ValueError("tile table too small for B=%d N=%d" % (B, N))
+        p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
+        st = fa_fwd_splitkv_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                   hkv, N, D, causal, scale, code, tiles.data_ptr(), num_splits, p, seed, offset,
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream_handle(q.device))
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_splitkv_masked")
+        return out, lse
     if dropout is not None:
         p, seed, offset = dropout
         st = fa_fwd_splitkv_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,

@@ -198,13 +198,15 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
-// The split-K/V forward for H_kv K/V heads, with dropout when drop_p >= 0.
+// The split-K/V forward for H_kv K/V heads, with dropout when drop_p >= 0 and
+// a key-padding mask when tiles is not NULL.
 int splitkv_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                    int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits,
-                   float drop_p, uint64_t seed, uint64_t offset, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+                   float drop_p, uint64_t seed, uint64_t offset, const void* tiles, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
   if (st != FA_OK) return st;
+  if (tiles && !aligned16(tiles)) return FA_ERR_ALIGN;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
   if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
   const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
@@ -218,8 +220,14 @@ int splitkv_common(const void* q, const void* k, const void* v, void* o, float* 
   a.part_lse = static_cast<float*>(workspace);
   a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return status_of(drop ? fa::launch_fwd_splitkv_dropout(a, static_cast<int>(D), causal != 0, dtype, s)
-                        : fa::launch_fwd_splitkv(a, static_cast<int>(D), causal != 0, dtype, s));
+  const int d = static_cast<int>(D);
+  const bool c = causal != 0;
+  if (tiles) {
+    a.mask = mask_tiles_view(tiles, B, N);
+    return status_of(drop ? fa::launch_fwd_splitkv_masked_dropout(a, d, c, dtype, s)
+                          : fa::launch_fwd_splitkv_masked(a, d, c, dtype, s));
+  }
+  return status_of(drop ? fa::launch_fwd_splitkv_dropout(a, d, c, dtype, s) : fa::launch_fwd_splitkv(a, d, c, dtype, s));
 }
 
 }  // namespace
@@ -278,15 +286,15 @@ int fa_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t D, int ca
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                    int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  return splitkv_common(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype, num_splits, -1.f, 0, 0, workspace,
-                        workspace_bytes, stream);
+  return splitkv_common(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype, num_splits, -1.f, 0, 0, nullptr,
+                        workspace, workspace_bytes, stream);
 }
 
 int fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                        int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, -1.f, 0, 0, workspace,
-                        workspace_bytes, stream);
+  return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, -1.f, 0, 0, nullptr,
+                        workspace, workspace_bytes, stream);
 }
 
 // ---- key-padding masks -----------------------------------------------------
@@ -400,7 +408,17 @@ int fa_fwd_splitkv_dropout(const void* q, const void* k, const void* v, void* o,
                            void* stream) {
   if (!(dropout_p >= 0.f)) return FA_ERR_UNSUPPORTED;  // NaN or negative; the rest as for the other dropout calls
   return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, dropout_p, seed, offset,
-                        workspace, workspace_bytes, stream);
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                          int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
+                          int num_splits, float dropout_p, uint64_t seed, uint64_t offset, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!tiles) return FA_ERR_NULL;
+  if (!(dropout_p >= 0.f)) return FA_ERR_UNSUPPORTED;
+  return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits,
+                        dropout_p > 0.f ? dropout_p : -1.f, seed, offset, tiles, workspace, workspace_bytes, stream);
 }
 
 int fa_fwd_masked_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,

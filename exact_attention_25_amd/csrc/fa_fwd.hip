@@ -64,6 +64,7 @@ struct FwdShape {
 };
 
 // SPLIT: the workgroup covers only key tiles [kt_begin, kt_end) of its split
+// (with MASK: its share of the list of non-empty tiles)
 // and writes FP32 partial states (O normalised within the range, and the
 // range's LSE) for merge_kernel instead of the final O and LSE.
 // MASK: a key-padding mask given by its block-level flags (a.mask): the
@@ -77,7 +78,6 @@ struct FwdShape {
 // SPLIT, each split's O; the merge weights are those of the undropped LSEs).
 template <int D, int QB, bool CAUSAL, class T, bool SPLIT, bool MASK, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdArgs a) {
-  static_assert(!(SPLIT && MASK), "split-K/V takes no mask");
   constexpr int BM = FwdShape<QB>::BM, BN = kFwdBN, NT = kFwdThreads;
   constexpr int RC = D / 8;              // 16-byte chunks per row
   constexpr int TC = BN * RC;            // chunks per K or V tile
@@ -139,7 +139,9 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
   int i_begin = 0, i_end;
   const int64_t b = MASK ? bh / a.H : 0;  // batch element (mask mode only)
   if constexpr (MASK) {
-    i_end = a.mask.prefix[b * (a.mask.n_tiles + 1) + n_kt];
+    const int i_all = a.mask.prefix[b * (a.mask.n_tiles + 1) + n_kt];
+    i_begin = SPLIT ? (int)(((int64_t)split * i_all) / a.n_splits) : 0;
+    i_end = SPLIT ? (int)(((int64_t)(split + 1) * i_all) / a.n_splits) : i_all;
   } else {
     i_begin = SPLIT ? (int)(((int64_t)split * n_kt_all) / a.n_splits) : 0;
     i_end = SPLIT ? min(n_kt, (int)(((int64_t)(split + 1) * n_kt_all) / a.n_splits)) : n_kt;
@@ -521,13 +523,13 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
     }
   } else if (i_begin < i_end) {  // workgroup-uniform
     TileWindow win;
-    win.init(a.mask.list + b * a.mask.n_tiles, a.mask.words + b * a.mask.n_tiles, i_end, lane);
+    win.init(a.mask.list + b * a.mask.n_tiles, a.mask.words + b * a.mask.n_tiles, i_end, lane, i_begin);
     // Tiles at positions i and i+1 (carried from step to step), their words.
-    int kt_c = win.tile(0, lane);
-    int kt_n = 1 < i_end ? win.tile(1, lane) : 0;
+    int kt_c = win.tile(i_begin, lane);
+    int kt_n = i_begin + 1 < i_end ? win.tile(i_begin + 1, lane) : 0;
     uint32_t w_lo, w_hi, wn_lo = 0, wn_hi = 0;
-    win.word(0, w_lo, w_hi);
-    if (1 < i_end) win.word(1, wn_lo, wn_hi);
+    win.word(i_begin, w_lo, w_hi);
+    if (i_begin + 1 < i_end) win.word(i_begin + 1, wn_lo, wn_hi);
     load_k(kt_c, lds_k0);
     load_v(kt_c, lds_v0);
     if (i_begin + 1 < i_end) load_k(kt_n, lds_k1);
@@ -690,12 +692,12 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(uint8_t* __restrict__
   }
 }
 
-template <int D, int QB, bool CAUSAL, class T, bool DROP>
+template <int D, int QB, bool CAUSAL, class T, bool MASK, bool DROP>
 hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
   constexpr int BM = FwdShape<QB>::BM;
   a.n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles * a.n_splits;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true, false, DROP>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, T, true, MASK, DROP>), dim3((unsigned)n_wg), dim3(kFwdThreads), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -777,7 +779,37 @@ hipError_t launch_dropout_mask(uint8_t* keep, int64_t BH, int64_t N, const Dropo
 
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_FWD_CASE(DD, CC, TT) \
-  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT, false>(a, stream);
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT, false, false>(a, stream);
+  FA_FWD_CASE(64, false, Fp16)
+  FA_FWD_CASE(64, true, Fp16)
+  FA_FWD_CASE(128, false, Fp16)
+  FA_FWD_CASE(128, true, Fp16)
+  FA_FWD_CASE(64, false, Bf16)
+  FA_FWD_CASE(64, true, Bf16)
+  FA_FWD_CASE(128, false, Bf16)
+  FA_FWD_CASE(128, true, Bf16)
+#undef FA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_splitkv_masked(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_FWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT, true, false>(a, stream);
+  FA_FWD_CASE(64, false, Fp16)
+  FA_FWD_CASE(64, true, Fp16)
+  FA_FWD_CASE(128, false, Fp16)
+  FA_FWD_CASE(128, true, Fp16)
+  FA_FWD_CASE(64, false, Bf16)
+  FA_FWD_CASE(64, true, Bf16)
+  FA_FWD_CASE(128, false, Bf16)
+  FA_FWD_CASE(128, true, Bf16)
+#undef FA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_splitkv_masked_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+#define FA_FWD_CASE(DD, CC, TT) \
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT, true, true>(a, stream);
   FA_FWD_CASE(64, false, Fp16)
   FA_FWD_CASE(64, true, Fp16)
   FA_FWD_CASE(128, false, Fp16)
@@ -792,7 +824,7 @@ hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, h
 
 hipError_t launch_fwd_splitkv_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
 #define FA_FWD_CASE(DD, CC, TT) \
-  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT, true>(a, stream);
+  if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_split_t<DD, kFwdQB, CC, TT, false, true>(a, stream);
   FA_FWD_CASE(64, false, Fp16)
   FA_FWD_CASE(64, true, Fp16)
   FA_FWD_CASE(128, false, Fp16)

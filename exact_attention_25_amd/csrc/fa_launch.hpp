@@ -124,6 +124,8 @@ hipError_t launch_fwd_dropout(const FwdArgs& a, int D, bool causal, int dtype, h
 hipError_t launch_bwd_dropout(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_fwd_masked_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_fwd_splitkv_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_fwd_splitkv_masked(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_fwd_splitkv_masked_dropout(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_bwd_masked_dropout(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 // keep[b][h][i][j] (bytes, 1 = kept) of the dropout mask, for tests.
 hipError_t launch_dropout_mask(uint8_t* keep, int64_t BH, int64_t N, const DropoutArgs& d, hipStream_t stream);

@@ -360,6 +360,22 @@ int fa_fwd_splitkv_dropout(const void* q, const void* k, const void* v, void* o,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_splitkv_masked -- the split-K/V forward (fa_fwd_splitkv_gqa) with a
+ * key-padding mask given by its tile table, as in fa_fwd_masked: each split
+ * takes its share of the batch element's list of non-empty key tiles, and a
+ * row that sees no key in a split gets the -inf partial LSE the merge
+ * weights by zero (a row with no visible key at all: O = 0, LSE = -inf).
+ * dropout_p = 0: no dropout; 0 < dropout_p < 1: dropout as in
+ * fa_fwd_masked_dropout.  Errors as for fa_fwd_splitkv_gqa and the dropout
+ * calls, plus FA_ERR_NULL / FA_ERR_ALIGN for the table.
+ */
+int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                          int causal, float scale, int dtype, const void* tiles, int num_splits,
+                          float dropout_p, uint64_t seed, uint64_t offset,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_dropout_mask -- write the keep mask the dropout calls above use:
  * keep[b][h][i][j] = 1 (kept) or 0 (dropped), bytes, [B, H, N, N] on the
  * device (caller-owned, any alignment).  Meant for tests and inspection: it

@@ -27,7 +27,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes",
                                     "fa_bwd_masked", "fa_bwd_masked_dropout", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
                                     "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_masked_dropout", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_num_splits",
+                                    "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_masked", "fa_fwd_splitkv_num_splits",
                                     "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
                                     "fa_status_str"]
 
@@ -277,3 +277,14 @@ def test_splitkv_gqa_rejects(kw, code):
     a.update(kw)
     assert fb.fa_fwd_splitkv_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["D"],
                                  a["causal"], a["scale"], a["dtype"], a["s"], a["ws"], a["wsb"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 4), 4), (dict(p=1.0), 3), (dict(p=-0.1), 3),
+                                     (dict(s=0), 3), (dict(ws=None), 5), (dict(Hkv=3), 2)])
+def test_splitkv_masked_rejects(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, Hkv=2, N=300, D=64, causal=1, scale=0.1, dtype=0, tiles=P, s=3,
+             p=0.0, seed=0, offset=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    assert fb.fa_fwd_splitkv_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
+                                    a["D"], a["causal"], a["scale"], a["dtype"], a["tiles"], a["s"], a["p"],
+                                    a["seed"], a["offset"], a["ws"], a["wsb"], None) == code

@@ -7,9 +7,9 @@ import torch
 
 import exact_attention_25_amd as fa
 from exact_attention_25_amd import workloads
-from exact_attention_25_amd.inputs import make_inputs, round_to
+from exact_attention_25_amd.inputs import make_inputs, make_key_mask, round_to
 from oracle import attention_forward
-from parity import assert_fwd_close, say, to_dev, to_host
+from parity import LSE_TOL, assert_fwd_close, o_error_ok, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -111,3 +111,33 @@ def test_splitkv_grouped_heads(with_dropout, causal, Hkv):
     torch.cuda.synchronize()
     o_ref, lse_ref = attention_forward(q, k, v, causal, 1 / np.sqrt(D), dropout=drop)
     assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, "fp16", "split gqa")
+
+
+@pytest.mark.parametrize("kind", ["lengths", "blocks", "random"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("with_dropout", [False, True])
+def test_splitkv_with_key_mask(with_dropout, D, causal, kind):
+    # each split walks its share of the list of non-empty tiles; rows that
+    # see no key in a split are weighted out by the merge, rows that see no
+    # key at all get O = 0 and LSE = -inf
+    B, H, Hkv, N = 2, 4, 2, 700
+    rng = np.random.default_rng(3400 + D + causal + with_dropout)
+    q = round_to(rng.standard_normal((B, H, N, D), dtype=np.float32), "bf16")
+    k = round_to(rng.standard_normal((B, Hkv, N, D), dtype=np.float32), "bf16")
+    v = round_to(rng.standard_normal((B, Hkv, N, D), dtype=np.float32), "bf16")
+    m = make_key_mask(B, N, kind, seed=3401 + causal, p=0.5)
+    if kind == "random":
+        m[:, :2] = 0
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    tiles = fa.mask_tiles(torch.from_numpy(m).cuda())
+    drop = (0.1, 5, 6) if with_dropout else None
+    o, lse = fa.fwd_splitkv(qd, kd, vd, 3, causal=causal, scale=0.1, tiles=tiles, dropout=drop)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_forward(q, k, v, causal, 0.1, key_mask=m, dropout=drop)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(to_host(lse)), empty)
+    full = ~empty
+    assert np.all(to_host(o)[empty] == 0)
+    assert o_error_ok(to_host(o)[full], o_ref[full], "bf16")[0]
+    assert np.abs(to_host(lse)[full] - lse_ref[full]).max() <= LSE_TOL
