@@ -634,3 +634,47 @@ def test_dropout_head_numbers_select_a_head_of_a_larger_problem():
     o, lse = attention_forward(q, k, v, False, 0.5, dropout=drop)
     o1, _ = attention_forward(q[1:2, 2:3], k[1:2, 2:3], v[1:2, 2:3], False, 0.5, dropout=drop + ([[1 * H + 2]],))
     assert np.array_equal(o[1:2, 2:3], o1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_dropout_brute_force_agrees(causal):
+    # a key-padding mask and dropout together: hidden keys leave the softmax,
+    # then the kept probabilities of the visible ones are scaled
+    n, d, p, seed, offset = 8, 3, 0.3, 91, 4
+    q, k, v = _rand(650, n, d), _rand(651, n, d), _rand(652, n, d)
+    vis = np.array([0, 0, 1, 1, 0, 1, 1, 0], dtype=np.uint8)
+    keep = dropout_keep(1, 1, n, p, seed, offset)[0, 0]
+    _, ks = dropout_threshold(p)
+    ob, lb = brute_force_forward(q.tolist(), k.tolist(), v.tolist(), causal, 0.7, visible=vis.tolist(),
+                                 keep=keep.tolist(), keep_scale=ks)
+    o, lse = attention_forward(_heads(q), _heads(k), _heads(v), causal, 0.7, key_mask=vis[None],
+                               dropout=(p, seed, offset))
+    fin = np.isfinite(np.array(lb))
+    assert np.abs(o[0, 0] - np.array(ob)).max() < 1e-14
+    assert np.abs(lse[0, 0][fin] - np.array(lb)[fin]).max() < 1e-14
+    assert np.array_equal(np.isneginf(lse[0, 0]), ~fin)  # causal rows 0 and 1 see only hidden keys
+    assert (~fin).sum() == (2 if causal else 0)
+
+
+def test_masked_dropout_backward_matches_finite_differences():
+    n, d = 6, 3
+    q, k, v = _rand(660, 1, 2, n, d), _rand(661, 1, 2, n, d), _rand(662, 1, 2, n, d)
+    do = _rand(663, 1, 2, n, d)
+    m = np.array([[1, 1, 0, 1, 0, 1]], dtype=np.uint8)
+    drop = (0.3, 4321, 1)
+    grads = attention_backward(q, k, v, do, True, 0.6, key_mask=m, dropout=drop)
+
+    def loss(q_, k_, v_):
+        return float((attention_forward(q_, k_, v_, True, 0.6, key_mask=m, dropout=drop)[0] * do).sum())
+
+    h = 1e-6
+    for gi, name in enumerate("qkv"):
+        base = [q, k, v]
+        num = np.zeros_like(base[gi])
+        for idx in np.ndindex(base[gi].shape):
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[gi][idx] += h
+            minus[gi][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        assert np.abs(num - grads[gi]).max() < 1e-8, name
