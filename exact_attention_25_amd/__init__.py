@@ -19,4 +19,7 @@ def __getattr__(name):
     if name in _BINDING_NAMES:
         from . import binding
         return getattr(binding, name)
+    if name == "attention":  # differentiable attention over fwd / bwd
+        from .autograd import attention
+        return attention
     raise AttributeError(name)
