@@ -57,5 +57,22 @@ def build(verbose=False, resource_usage=False, out=LIB_PATH):
     return out
 
 
+def build_c_client(verbose=False):
+    """Compile tests/c_abi_client.cpp (a torch-free client of the C ABI) into
+    tests/c_abi_client, linked against libfa.so by its in-tree path."""
+    src = os.path.join(ROOT, "tests", "c_abi_client.cpp")
+    out = os.path.join(ROOT, "tests", "c_abi_client")
+    cmd = [HIPCC, "-O2", "-std=c++17", "-I" + INCLUDE, src, "-o", out + ".tmp",
+           "-L" + PKG_DIR, "-lfa", "-Wl,-rpath," + PKG_DIR]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building the C ABI client")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True, resource_usage="--resource-usage" in sys.argv)
