@@ -288,3 +288,23 @@ def test_splitkv_masked_rejects(kw, code):
     assert fb.fa_fwd_splitkv_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
                                     a["D"], a["causal"], a["scale"], a["dtype"], a["tiles"], a["s"], a["p"],
                                     a["seed"], a["offset"], a["ws"], a["wsb"], None) == code
+
+
+CLIENT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_client")
+
+
+def test_c_client_argument_errors(tmp_path):
+    """The torch-free client (built by build()) links against libfa.so and
+    rejects bad invocations before any GPU call: exit 2 with a message."""
+    import subprocess
+    if not os.path.exists(CLIENT):
+        pytest.skip("tests/c_abi_client is not built (build() compiles it)")
+    res = subprocess.run([CLIENT], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 2 and "usage" in res.stderr
+    missing = str(tmp_path / "absent.bin")
+    res = subprocess.run([CLIENT, missing, str(tmp_path / "o.bin"), "1", "1", "64", "64", "0", "0", "0.125"],
+                         capture_output=True, text=True, timeout=60)
+    assert res.returncode == 2 and "cannot read" in res.stderr
+    res = subprocess.run([CLIENT, missing, str(tmp_path / "o.bin"), "1", "0", "64", "64", "0", "0", "0.125"],
+                         capture_output=True, text=True, timeout=60)
+    assert res.returncode == 2
