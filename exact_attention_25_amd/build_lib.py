@@ -41,18 +41,33 @@ def hipcc_flags(resource_usage=False):
     return flags
 
 
-def build(verbose=False, resource_usage=False, out=LIB_PATH):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + hipcc_flags(resource_usage) + srcs + ["-o", tmp]
+def _run(cmd, verbose, show_stderr, what):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libfa.so")
-    if resource_usage or verbose:
+        raise RuntimeError("hipcc failed: " + what)
+    if show_stderr:
         sys.stderr.write(res.stderr)
+
+
+def build(verbose=False, resource_usage=False, out=LIB_PATH):
+    """Compile every source to an object in parallel (one hipcc each), then
+    link libfa.so; the library is replaced only when everything succeeded."""
+    from concurrent.futures import ThreadPoolExecutor
+    import tempfile
+
+    compile_flags = [f for f in hipcc_flags(resource_usage) if f != "-shared"]
+    tmp = out + ".tmp%d" % os.getpid()
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as d:
+        objs = [os.path.join(d, s + ".o") for s in SOURCES]
+        jobs = [([HIPCC] + compile_flags + ["-c", os.path.join(CSRC, s), "-o", o], s) for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as pool:
+            for f in [pool.submit(_run, cmd, verbose, resource_usage or verbose, s) for cmd, s in jobs]:
+                f.result()
+        _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp], verbose, verbose,
+             "linking libfa.so")
     os.replace(tmp, out)
     return out
 
