@@ -247,8 +247,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_ker
   };
   auto put_rows = [&](float* ll, float* ld) {
     if (tid < BQ) {
-      ll[tid] = lse_n;
-      ld[tid] = dl_n;
+      // The byte offset is made opaque so that it is formed here rather than
+      // kept per buffer in live registers across the loop.
+      int t4 = tid * 4;
+      asm volatile("" : "+v"(t4));
+      *(float*)((char*)ll + t4) = lse_n;
+      *(float*)((char*)ld + t4) = dl_n;
     }
   };
 
@@ -545,17 +549,17 @@ __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_ker
       if (CAUSAL && qb0 + 31 < k0w) continue;  // every query precedes every key
       // Offsets opaque per block: the XORed offsets are formed beside their
       // reads instead of being hoisted out of the loop into live registers.
-      uint32_t rb = roff0, tb0 = toff0, tb1 = toff1;
-      asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));
+      uint32_t rb = roff0, tb0 = toff0, tb1 = toff1, g32 = g * 32;
+      asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1), "+v"(g32));
       // Register r holds query qb*32 + acc_row(r, g): two runs of 8.
       f32x16 s, dp;
-      const f32x4* lse4 = (const f32x4*)ll;
-      const f32x4* dl4 = (const f32x4*)ld;
+      const f32x4* lse4 = (const f32x4*)((const char*)ll + g32);
+      const f32x4* dl4 = (const f32x4*)((const char*)ld + g32);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int v4 = 0; v4 < 2; ++v4) {
-          const int idx = (qb * 32 + h * 16 + g * 8) / 4 + v4;
+          const int idx = (qb * 32 + h * 16) / 4 + v4;
           const f32x4 x = lse4[idx], y = dl4[idx];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
