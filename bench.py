@@ -102,10 +102,12 @@ def load_traffic(workload_name, launches_per_step=1):
 
 def cpu_baseline(w, seconds):
     """Time the float64 oracle on whole heads of the workload until about
-    `seconds` have passed; report algorithmic TFLOP/s on that sample."""
+    `seconds` have passed; report algorithmic TFLOP/s on that sample.  For a
+    forward+backward workload the oracle's backward is timed the same way
+    (its own heads, its own time budget) and reported under "bwd"."""
     import numpy as np
     from exact_attention_25_amd.inputs import make_inputs
-    from oracle import attention_forward
+    from oracle import attention_backward, attention_forward
     blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
@@ -114,26 +116,45 @@ def cpu_baseline(w, seconds):
         blas = ",".join(sorted({i.get("internal_api", "?") for i in pools})) or "none"
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    heads_done, t_total = 0, 0.0
-    per_head = w.fwd_flops() / (w.B * w.H)
     order = [(b, h) for b in range(w.B) for h in range(w.H)]
-    for b, h in order:
-        inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys, heads=[(b, h)])
-        q, k, v = (inp[n][None] for n in ("q", "k", "v"))
-        t0 = time.perf_counter()
-        attention_forward(q, k, v, w.causal, w.scale)
-        t_total += time.perf_counter() - t0
-        heads_done += 1
-        if t_total >= seconds:
-            break
-    return {
-        "value": heads_done * per_head / t_total / 1e12,
+
+    def time_heads(fn, flops_per_head, with_dout):
+        heads_done, t_total = 0, 0.0
+        for b, h in order:
+            inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys, heads=[(b, h)],
+                              with_dout=with_dout)
+            args = [inp[n][None] for n in (("q", "k", "v", "do") if with_dout else ("q", "k", "v"))]
+            t0 = time.perf_counter()
+            fn(*args)
+            t_total += time.perf_counter() - t0
+            heads_done += 1
+            if t_total >= seconds:
+                break
+        return heads_done * flops_per_head / t_total / 1e12, heads_done, t_total
+
+    value, heads_done, t_total = time_heads(lambda q, k, v: attention_forward(q, k, v, w.causal, w.scale),
+                                            w.fwd_flops() / (w.B * w.H), False)
+    rec = {
+        "value": value,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "sample": "%d of %d heads of %s, float64 numpy (BLAS %s, %d host CPUs available), %.1f s" % (
             heads_done, len(order), w.name, blas, len(os.sched_getaffinity(0)), t_total),
     }
+    if w.backward:
+        value, heads_done, t_total = time_heads(
+            lambda q, k, v, do: attention_backward(q, k, v, do, w.causal, w.scale), w.bwd_flops() / (w.B * w.H), True)
+        rec["bwd"] = {
+            "value": value,
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "kind": "oracle",
+            "flops_counted": "10*B*H*N^2*D (causal: half), the GPU backward's count",
+            "sample": "attention_backward on %d of %d heads of %s, float64 numpy (BLAS %s), %.1f s" % (
+                heads_done, len(order), w.name, blas, t_total),
+        }
+    return rec
 
 
 def main():

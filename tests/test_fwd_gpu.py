@@ -35,7 +35,7 @@ def test_fwd_small(B, H, N, D, causal, dtype):
     assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, dtype, "N=%d D=%d" % (N, D))
 
 
-# ---- the workloads at full size, compared on sampled heads / rows ----
+# ---- the workloads at full size: every head against the oracle ----
 def _sample_rows(n, count, rng):
     base = np.unique(np.concatenate([np.arange(0, min(n, 64)), np.arange(max(0, n - 64), n),
                                      np.arange(0, n, 64)[:64]]))
@@ -49,20 +49,27 @@ WORKLOADS = [workloads.SMALL, workloads.NONCAUSAL_D64, *workloads.CAUSAL_D128.va
 
 @pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
 def test_fwd_workload(w):
+    """The whole output of every head against the oracle (the golden-reference
+    comparison of "FlashAttention dataflow and engineering validation on
+    MI50", §5.1).  The long bf16 workload (N = 32768) compares 512 sampled
+    query rows -- the first and last 64, every 64th, the rest random -- of
+    every one of its heads."""
     say("fwd workload %s" % w.name)
     inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys)
     o, lse = run_fwd(inp, w.dtype, w.causal, w.scale)
     rng = np.random.default_rng(w.seed)
-    heads = sorted(set([(0, 0), (w.B - 1, w.H - 1)] + [(0, int(h)) for h in rng.choice(w.H, size=min(w.H, 2), replace=False)]))
     rows = None if w.N <= 8192 else _sample_rows(w.N, 512, rng)
-    for b, h in heads:
-        qh, kh, vh = (inp[n][b:b + 1, h:h + 1] for n in ("q", "k", "v"))
-        o_ref, lse_ref = attention_forward(qh, kh, vh, w.causal, w.scale, rows=rows)
-        og = to_host(o[b:b + 1, h:h + 1])
-        lg = to_host(lse[b:b + 1, h:h + 1])
-        if rows is not None:
-            og, lg = og[:, :, rows], lg[:, :, rows]
-        assert_fwd_close(og, lg, o_ref, lse_ref, w.dtype, "%s head (%d,%d)" % (w.name, b, h))
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], w.causal, w.scale, rows=rows)
+    og, lg = to_host(o), to_host(lse)
+    if rows is not None:
+        og, lg = og[:, :, rows], lg[:, :, rows]
+    assert_fwd_close(og, lg, o_ref, lse_ref, w.dtype, "%s, all %d heads%s" % (
+        w.name, w.B * w.H, "" if rows is None else ", %d rows each" % rows.size))
+    if w.dtype == "bf16":  # the literal figures beside the per-element bound
+        o_ref_b = round_to(o_ref.astype(np.float32), "bf16").astype(np.float64)
+        say("  literal max abs error %.3e; against bf16(O_ref) %.3e" % (
+            np.abs(og - o_ref).max(), np.abs(og - o_ref_b).max()))
+    del o_ref, lse_ref
     # properties over the whole output
     on = to_host(o)
     assert np.all(np.isfinite(on))
