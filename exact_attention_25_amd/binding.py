@@ -106,6 +106,9 @@ def load_library():
     lib.fa_bwd_masked_dropout.restype = ctypes.c_int
     lib.fa_dropout_mask.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_float, _u64, _u64, _vp]
     lib.fa_dropout_mask.restype = ctypes.c_int
+    lib.fa_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp]
+    lib.fa_bwd_noalloc.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -125,6 +128,11 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype,
            workspace, workspace_bytes, stream):
     return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, int(causal),
                                  float(scale), int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, stream):
+    return load_library().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, int(causal),
+                                         float(scale), int(dtype), stream)
 
 
 def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, stream):

@@ -182,6 +182,23 @@ int check_fwd(const void* q, const void* k, const void* v, void* o, float* lse, 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
               void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, int causal,
               float scale, int dtype, void* workspace, size_t workspace_bytes) {
+  const int st = fa::check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  const size_t need = bwd_workspace_layout(B, H, H_kv, N, D);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+namespace fa {
+
+int check_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                   int causal, float scale, int dtype) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_common(B, H, N, D, causal, scale, dtype);
   if (st != FA_OK) return st;
@@ -190,13 +207,12 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
-  const size_t need = bwd_workspace_layout(B, H, H_kv, N, D);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_ALIGN;
   return FA_OK;
 }
 
-int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+}  // namespace fa
+
+namespace {
 
 // The split-K/V forward for H_kv K/V heads, with dropout when drop_p >= 0 and
 // a key-padding mask when tiles is not NULL.
@@ -245,6 +261,9 @@ const char* fa_status_str(int status) {
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
+    case FA_ERR_SCRATCH_LIMIT:
+      return "FA_ERR_SCRATCH_LIMIT: the shape needs more backward workspace than the static scratch of "
+             "fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown fa_status";
   }
 }

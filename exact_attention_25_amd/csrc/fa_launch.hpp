@@ -115,6 +115,12 @@ inline int bwd_dq_parts(int64_t B, int64_t H, int64_t N) {
   return (int)(parts < cap ? parts : (cap > 1 ? cap : 1));
 }
 
+// Argument checks of the backward entry points other than the workspace:
+// FA_OK or an fa_status code (defined with the C ABI).
+int check_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
+                   int causal, float scale, int dtype);
+
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);

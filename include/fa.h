@@ -68,7 +68,9 @@ typedef enum fa_status {
   FA_ERR_UNSUPPORTED = 3, /* D, dtype, causal flag or scale unsupported          */
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
   FA_ERR_WORKSPACE = 5,   /* backward workspace missing or smaller than needed   */
-  FA_ERR_HIP = 6          /* the HIP runtime rejected a launch                   */
+  FA_ERR_HIP = 6,         /* the HIP runtime rejected a launch                   */
+  FA_ERR_SCRATCH_LIMIT = 7 /* fa_bwd_noalloc: the shape needs more workspace than
+                              the library's static scratch holds                */
 } fa_status;
 
 typedef enum fa_dtype { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
@@ -191,6 +193,32 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int64_t B, int64_t H, int64_t N, int64_t D,
            int causal, float scale, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, kernels and results as fa_bwd, with
+ * the workspace taken from the library's own static device scratch of
+ * FA_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends) instead of
+ * a caller's buffer.  It allocates and frees nothing.
+ *   Arguments : as for fa_bwd, without workspace and workspace_bytes.
+ *   Limit     : shapes with fa_bwd_workspace_bytes(...) above
+ *               FA_NOALLOC_SCRATCH_BYTES (e.g. more than 8M query rows B*H*N,
+ *               or few heads of a long sequence, whose partial dK/dV sums
+ *               need more) are rejected with FA_ERR_SCRATCH_LIMIT before any
+ *               work is enqueued.
+ *   Sharing   : every call on one GPU uses that GPU's one scratch array, so
+ *               calls that overlap on one GPU (on different streams or from
+ *               different threads) race; serialise them.  The scratch is the
+ *               one of the GPU `stream` belongs to.
+ * Returns FA_OK, FA_ERR_SCRATCH_LIMIT or another fa_status error code.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv,
+                   int64_t B, int64_t H, int64_t N, int64_t D,
+                   int causal, float scale, int dtype, void* stream);
 
 /*
  * fa_bwd_gqa_workspace_bytes -- bytes of device workspace fa_bwd_gqa and

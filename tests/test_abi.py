@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes",
-                                    "fa_bwd_masked", "fa_bwd_masked_dropout", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
+                                    "fa_bwd_masked", "fa_bwd_masked_dropout", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
                                     "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_masked_dropout", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_masked", "fa_fwd_splitkv_num_splits",
                                     "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert fb.status_str(0) == "FA_OK"
-    for code in range(1, 7):
+    for code in range(1, 8):
         assert fb.status_str(code).startswith("FA_ERR_")
     assert "unknown" in fb.status_str(99)
 
@@ -308,3 +308,26 @@ def test_c_client_argument_errors(tmp_path):
     res = subprocess.run([CLIENT, missing, str(tmp_path / "o.bin"), "1", "0", "64", "64", "0", "0", "0.125"],
                          capture_output=True, text=True, timeout=60)
     assert res.returncode == 2
+
+
+def test_bwd_noalloc_argument_errors_and_scratch_limit():
+    """fa_bwd_noalloc checks its arguments like fa_bwd, then rejects shapes
+    whose workspace exceeds its static scratch (32 MiB) with
+    FA_ERR_SCRATCH_LIMIT -- all before any GPU call."""
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, N=128, D=64, causal=1,
+                 scale=0.125, dtype=0)
+        a.update(kw)
+        return fb.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                 a["B"], a["H"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"], None)
+    assert call(dq=None) == 1
+    assert call(N=0) == 2
+    assert call(D=96) == 3
+    assert call(dv=P + 2) == 4
+    # Delta alone: 4 bytes per query row -- 8M rows fill the scratch exactly
+    assert fb.bwd_workspace_bytes(1, 64, 1 << 17, 64, 1, 0) == 32 << 20
+    assert call(B=1, H=65, N=1 << 17, D=64) == 7
+    # one head of 65536 rows: partial dK/dV and dQ sums of 64 MiB each
+    assert fb.bwd_workspace_bytes(1, 1, 1 << 16, 128, 1, 0) > 32 << 20
+    assert call(B=1, H=1, N=1 << 16, D=128) == 7
+    assert "scratch" in fb.status_str(7)
