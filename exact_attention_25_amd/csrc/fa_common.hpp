@@ -72,14 +72,21 @@ __device__ __forceinline__ uint32_t pack2<Bf16>(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// acc + lo + hi of a packed pair of 16-bit values, in FP32 (one v_dot2).
+// acc + lo + hi of a packed pair of 16-bit values, in FP32.
 template <class T>
 __device__ __forceinline__ float add_pair(uint32_t w, float acc);
 
+// fp16: two v_fma_mix_f32 (each half widened exactly, times 1.0, added with
+// one FP32 rounding).  These run on the vector ALU beside an MFMA; a v_dot2
+// would wait for the matrix core (measured on gfx950: a dependent v_dot2c per
+// 32x32x16 MFMA stretches it from 33 to 48 cycles).
 template <>
 __device__ __forceinline__ float add_pair<Fp16>(uint32_t w, float acc) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), h2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(acc)
+      : "v"(w));
+  return acc;
 }
 
 template <>

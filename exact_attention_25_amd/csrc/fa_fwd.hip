@@ -711,6 +711,7 @@ hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
+  if (D == 128) return launch_fwd_d128(a, causal, dtype, stream);
 #define FA_FWD_CASE(DD, CC, TT) \
   if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_t<DD, kFwdQB, CC, TT>(a, stream);
   FA_FWD_CASE(64, false, Fp16)
