@@ -120,3 +120,41 @@ def test_ragged_matches_padded_prefix():
     torch.cuda.synchronize()
     assert torch.allclose(o_cut.float(), o_full[:, :, :N].float(), atol=2e-3, rtol=0)
     assert torch.allclose(lse_cut, lse_full[:, :, :N], atol=1e-4, rtol=0)
+
+
+def nan_tailed(shape, dtype):
+    """A tensor at the start of a buffer that continues with 64 rows of NaN
+    (more than any tile reaches past the last row): a kernel that reads a
+    row past the end gets NaN into its result (0 * NaN is NaN in a product)."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 64 * shape[-1],), float("nan"), dtype=dtype, device="cuda")
+    return buf[:n].view(*shape)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("N", [17, 1000])
+def test_rows_past_the_end_are_never_read(N, D, causal, dtype):
+    """The partial last K/V tile of the last head is followed by memory that
+    is not the caller's: only its valid rows may reach the result.  Every
+    input sits at the start of a buffer that continues with NaN, and
+    fa_fwd, fa_fwd_splitkv and fa_bwd must still match the oracle."""
+    say("rows past the end N=%d D=%d causal=%d %s" % (N, D, causal, dtype))
+    inp = make_inputs(1, 2, N, D, dtype, seed=4500 + N + D, with_dout=True)
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = (nan_tailed(inp[n].shape, TORCH_DTYPE[dtype]).copy_(to_dev(inp[n], dtype))
+                   for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], causal, scale)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, dtype, "fa_fwd N=%d D=%d" % (N, D))
+    o2, lse2 = fa.fwd_splitkv(q, k, v, 3, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert_fwd_close(to_host(o2), to_host(lse2), o_ref, lse_ref, dtype, "fa_fwd_splitkv N=%d D=%d" % (N, D))
+    o_t = nan_tailed(o.shape, o.dtype).copy_(o)
+    lse_t = nan_tailed(lse.shape + (1,), torch.float32).view(lse.shape).copy_(lse)
+    grads = fa.bwd(q, k, v, o_t, lse_t, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
+    assert_grads_close([to_host(t) for t in grads], ref, "fa_bwd N=%d D=%d" % (N, D))
