@@ -350,6 +350,100 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// ---------------------------------------------------------------------------
+// MFMAs with explicit register classes (inline assembly).  The compiler
+// assigns MFMA accumulators to one register class per kernel; kernels that
+// need more than 256 live registers per wave place operands by hand: scores
+// in VGPRs, Q fragments and O accumulators in AGPRs.  Inline assembly is
+// opaque to the compiler's hazard checks, so the wait states gfx950 requires
+// are placed by hand: 12 between an MFMA that writes a register and a vector
+// instruction that reads it (scores_ready and o_ready give 16), and 2 between
+// a vector write and an MFMA reading that register as an operand (FRESH).
+// The register allocator may itself add such a write (a copy back from a
+// register parked in the other class) right before an MFMA; the generated
+// code of every kernel that uses these helpers is scanned for both hazards
+// by the test suite.
+// ---------------------------------------------------------------------------
+// S (VGPR) = A (VGPR) * B (AGPR), accumulator started at zero.  FRESH:
+// two wait states go first, for an operand that a vector instruction may
+// have written just before (including copies the register allocator adds).
+template <class T, bool FRESH = false>
+__device__ __forceinline__ void mfma_s_first(f32x16& d, const u32x4& a, const u32x4& b) {
+  if constexpr (T::id == Fp16::id) {
+    if constexpr (FRESH)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    else
+      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  } else {
+    if constexpr (FRESH)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  }
+}
+// S (VGPR) += A (VGPR) * B (AGPR).
+template <class T, bool FRESH = false>
+__device__ __forceinline__ void mfma_s_acc(f32x16& d, const u32x4& a, const u32x4& b) {
+  if constexpr (T::id == Fp16::id) {
+    if constexpr (FRESH)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    else
+      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  } else {
+    if constexpr (FRESH)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  }
+}
+// O (AGPR) += A (VGPR) * B (VGPR); FRESH: B was just written by vector
+// instructions, so two wait states go first.
+template <class T, bool FRESH>
+__device__ __forceinline__ void mfma_o(f32x16& d, const u32x4& a, const u32x4& b) {
+  if constexpr (T::id == Fp16::id) {
+    if constexpr (FRESH)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+    else
+      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  } else {
+    if constexpr (FRESH)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  }
+}
+// 16 wait states after MFMAs that wrote the four score accumulators of a
+// tile, before any vector instruction reads them (ties them so that no read
+// is scheduled above).
+__device__ __forceinline__ void scores_ready(f32x16 (&s)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+}
+__device__ __forceinline__ void scores_ready(f32x16 (&s)[1][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]));
+}
+// Workgroup barrier without the memory fence __syncthreads adds (which
+// waits for every load in flight, the tile copies included).  Callers wait
+// for exactly the copies the barrier must cover; the memory clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16 wait states after the last MFMA into O, before vector reads of O
+// (one or two query blocks, head size 128 or 64).
+__device__ __forceinline__ void o_ready(f32x16 (&o)[2][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7"
+               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]), "+a"(o[1][0]), "+a"(o[1][1]),
+                 "+a"(o[1][2]), "+a"(o[1][3]));
+}
+__device__ __forceinline__ void o_ready(f32x16 (&o)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
+}
+__device__ __forceinline__ void o_ready(f32x16 (&o)[1][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]));
+}
+__device__ __forceinline__ void o_ready(f32x16 (&o)[1][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]));
+}
+
 // Wave-uniform votes (every lane of the wave is active where these are used).
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 __device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }

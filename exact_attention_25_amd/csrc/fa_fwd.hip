@@ -710,8 +710,17 @@ hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
 
 }  // namespace
 
+// Which forward runs is set by how many workgroups it would launch (256
+// compute units): with fewer 128-query tiles than compute units, the
+// key-split forward of fa_fwd_short.hip; at D = 128 with at least
+// kD128From 256-query tiles, the 64-queries-per-wave kernel; otherwise this
+// file's 128-query kernel (thresholds from measured sweeps over N and H).
+constexpr int64_t kShortBelow = 256;
+constexpr int64_t kD128From = 1024;
+
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
-  if (D == 128) return launch_fwd_d128(a, causal, dtype, stream);
+  if ((int64_t)a.BH * ((a.N + 127) / 128) < kShortBelow) return launch_fwd_short(a, D, causal, dtype, stream);
+  if (D == 128 && (int64_t)a.BH * ((a.N + 255) / 256) >= kD128From) return launch_fwd_d128(a, causal, dtype, stream);
 #define FA_FWD_CASE(DD, CC, TT) \
   if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_t<DD, kFwdQB, CC, TT>(a, stream);
   FA_FWD_CASE(64, false, Fp16)

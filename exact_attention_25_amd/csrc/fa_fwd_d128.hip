@@ -57,57 +57,6 @@ constexpr int kPV = 3;                   // V^T fragments read ahead of their MF
 // the barrier waits only for the older ones.
 constexpr int kCopiesBeforeBarrier = 8;
 
-// S (VGPR) = A (VGPR) * B (AGPR), accumulator started at zero.
-template <class T>
-__device__ __forceinline__ void mfma_s_first(f32x16& d, const u32x4& a, const u32x4& b) {
-  if constexpr (T::id == Fp16::id)
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-  else
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-}
-// S (VGPR) += A (VGPR) * B (AGPR).
-template <class T>
-__device__ __forceinline__ void mfma_s_acc(f32x16& d, const u32x4& a, const u32x4& b) {
-  if constexpr (T::id == Fp16::id)
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-  else
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-// O (AGPR) += A (VGPR) * B (VGPR); FRESH: B was just written by vector
-// instructions, so two wait states go first.
-template <class T, bool FRESH>
-__device__ __forceinline__ void mfma_o(f32x16& d, const u32x4& a, const u32x4& b) {
-  if constexpr (T::id == Fp16::id) {
-    if constexpr (FRESH)
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-    else
-      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-  } else {
-    if constexpr (FRESH)
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-    else
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-  }
-}
-// 16 wait states after MFMAs that wrote the four score accumulators of a
-// tile, before any vector instruction reads them (ties them so that no read
-// is scheduled above).
-__device__ __forceinline__ void scores_ready(f32x16 (&s)[2][2]) {
-  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
-}
-// Workgroup barrier without the memory fence __syncthreads adds (which
-// waits for every load in flight, the tile copies included).  Callers wait
-// for exactly the copies the barrier must cover; the memory clobber keeps
-// the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-
-// 16 wait states after the last MFMA into O, before vector reads of O.
-__device__ __forceinline__ void o_ready(f32x16 (&o)[2][4]) {
-  asm volatile("s_nop 7\n\ts_nop 7"
-               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]), "+a"(o[1][0]), "+a"(o[1][1]),
-                 "+a"(o[1][2]), "+a"(o[1][3]));
-}
-
 template <class T, bool CAUSAL>
 __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
   // LDS: four K and four V tile buffers of 16 KB.  Tile t of K lives in K

@@ -124,6 +124,9 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o, c
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 // The forward at D = 128 with 64 queries per wave (fa_fwd_d128.hip).
 hipError_t launch_fwd_d128(const FwdArgs& a, bool causal, int dtype, hipStream_t stream);
+// The forward for small launches: 32 queries per workgroup, keys split over
+// its four waves (fa_fwd_short.hip).
+hipError_t launch_fwd_short(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 hipError_t launch_fwd_masked(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);

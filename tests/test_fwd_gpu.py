@@ -35,6 +35,24 @@ def test_fwd_small(B, H, N, D, causal, dtype):
     assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, dtype, "N=%d D=%d" % (N, D))
 
 
+# ---- launches smaller than the chip: the key-split forward ----
+# Fewer 128-query tiles than compute units select fa_fwd_short.hip: 32 or 64
+# queries per workgroup, keys split over its four waves, partial states
+# merged in LDS.  The shapes cover two workgroups sharing a CU (D = 64: 512
+# workgroups), ragged N, and long key walks (many passes over the V ring).
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,D", [(1, 32, 512, 64), (1, 32, 512, 128), (2, 8, 1000, 128), (1, 4, 2500, 64),
+                                     (1, 2, 4000, 128)])
+def test_fwd_small_grid(B, H, N, D, causal, dtype):
+    say("fwd small grid B=%d H=%d N=%d D=%d causal=%d %s" % (B, H, N, D, causal, dtype))
+    inp = make_inputs(B, H, N, D, dtype, seed=1500 + N + D + H)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = run_fwd(inp, dtype, causal, scale)
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], causal, scale)
+    assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, dtype, "B=%d H=%d N=%d D=%d" % (B, H, N, D))
+
+
 # ---- the workloads at full size: every head against the oracle ----
 def _sample_rows(n, count, rng):
     base = np.unique(np.concatenate([np.arange(0, min(n, 64)), np.arange(max(0, n - 64), n),

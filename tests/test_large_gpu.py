@@ -42,15 +42,17 @@ def test_heads_beyond_2g_elements():
     torch.cuda.synchronize()
 
     # head (2, 648) is batch-head 2048: its first element is at 2^31.  Each
-    # sampled head is recomputed as 16 copies of itself: that gives the dK/dV
-    # pass 1024 workgroups, so, as in the large call, it does not split the
-    # head's query tiles into parts (parts would add FP32 partial sums in
-    # another order); copy 0 must equal the large call's head bitwise.
+    # sampled head is recomputed as 32 copies of itself: that gives the
+    # forward 1024 tiles of 256 queries, so it runs the same kernel as the
+    # large call, and the dK/dV pass 2048 workgroups, so, as in the large
+    # call, it does not split the head's query tiles into parts (parts would
+    # add FP32 partial sums in another order); copy 0 must equal the large
+    # call's head bitwise.
     for b, h in ((0, 0), (1, 347), (2, 647), (2, 648), (2, 699)):
         say("large: head (%d, %d) alone" % (b, h))
         sl = (slice(b, b + 1), slice(h, h + 1))
-        qh, kh, vh, doh = (t[sl].expand(1, 16, N, D).contiguous() for t in (q, k, v, do))
-        assert fa.bwd_workspace_bytes(1, 16, N, D, 1, 0) == 16 * N * 4  # one part
+        qh, kh, vh, doh = (t[sl].expand(1, 32, N, D).contiguous() for t in (q, k, v, do))
+        assert fa.bwd_workspace_bytes(1, 32, N, D, 1, 0) == 32 * N * 4  # one part
         o1, l1 = fa.fwd(qh, kh, vh, causal=True, scale=scale)
         g1 = fa.bwd(qh, kh, vh, o1, l1, doh, causal=True, scale=scale)
         torch.cuda.synchronize()
