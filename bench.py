@@ -54,7 +54,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # limit", §8) = 2*1*32*8192^2*128 FLOP / 25.854 ms = 21.26 TFLOP/s.
 PAGE_BASELINE_TFLOPS = 2 * 32 * 8192 ** 2 * 128 / 25.854e-3 / 1e12
 
-FWD_SOURCES = ["exact_attention_25_amd/csrc/fa_fwd.hip", "exact_attention_25_amd/csrc/fa_common.hpp"]
+FWD_SOURCES = ["exact_attention_25_amd/csrc/fa_fwd.hip", "exact_attention_25_amd/csrc/fa_fwd_d128.hip",
+               "exact_attention_25_amd/csrc/fa_fwd_short.hip", "exact_attention_25_amd/csrc/fa_common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_causal_b1h32n8192d128_fp16_traffic.json")
 
 
@@ -339,7 +340,8 @@ def main():
     elif args.splits > 0:
         kernel = "fwd_kernel<%d,%s> split x%d + merge_kernel" % (w.D, "causal" if w.causal else "full", args.splits)
     else:
-        kernel = "fwd_kernel<%d,%s>" % (w.D, "causal" if w.causal else "full")
+        kernel = "%s<%d,%s,%s>" % (fa.fwd_kernel_name(w.B, w.H, w.N, w.D, w.causal), w.D,
+                                   "causal" if w.causal else "full", w.dtype)
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),

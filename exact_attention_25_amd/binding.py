@@ -64,6 +64,8 @@ def load_library():
     lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_splitkv_num_splits.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
     lib.fa_fwd_splitkv_num_splits.restype = ctypes.c_int
+    lib.fa_fwd_kernel_name.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.fa_fwd_kernel_name.restype = ctypes.c_char_p
     lib.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_gqa_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
@@ -159,6 +161,11 @@ def fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits):
 def splitkv_num_splits(B, H, N, D, causal):
     """fa_fwd_splitkv_num_splits: the library's split count for a shape."""
     return int(load_library().fa_fwd_splitkv_num_splits(B, H, N, D, int(causal)))
+
+
+def fwd_kernel_name(B, H, N, D, causal):
+    """fa_fwd_kernel_name: the forward kernel fa_fwd runs for this shape."""
+    return load_library().fa_fwd_kernel_name(B, H, N, D, int(causal)).decode()
 
 
 def bwd_workspace_bytes(B, H, N, D, causal, dtype):

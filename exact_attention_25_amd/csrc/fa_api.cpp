@@ -291,6 +291,18 @@ size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D
   return align256(rows * sizeof(float)) + align256(rows * static_cast<size_t>(D) * sizeof(float));
 }
 
+const char* fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int causal) {
+  if (check_common(B, H, N, D, causal, 1.0f, FA_FP16) != FA_OK) return "";
+  switch (fa::fwd_path(B * H, N, D)) {
+    case fa::FwdPath::kShort:
+      return "fwd_short_kernel";
+    case fa::FwdPath::kD128:
+      return "fwd_d128_kernel";
+    default:
+      return "fwd_kernel";
+  }
+}
+
 int fa_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t D, int causal) {
   if (check_common(B, H, N, D, causal, 1.0f, FA_FP16) != FA_OK) return 0;
   // Measured on MI355X (fp16, D = 128): B1 H1 N16384 runs at 481 TFLOP/s in

@@ -718,9 +718,16 @@ hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
 constexpr int64_t kShortBelow = 256;
 constexpr int64_t kD128From = 1024;
 
+FwdPath fwd_path(int64_t BH, int64_t N, int64_t D) {
+  if (BH * ((N + 127) / 128) < kShortBelow) return FwdPath::kShort;
+  if (D == 128 && BH * ((N + 255) / 256) >= kD128From) return FwdPath::kD128;
+  return FwdPath::kTiled;
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
-  if ((int64_t)a.BH * ((a.N + 127) / 128) < kShortBelow) return launch_fwd_short(a, D, causal, dtype, stream);
-  if (D == 128 && (int64_t)a.BH * ((a.N + 255) / 256) >= kD128From) return launch_fwd_d128(a, causal, dtype, stream);
+  const FwdPath path = fwd_path(a.BH, a.N, D);
+  if (path == FwdPath::kShort) return launch_fwd_short(a, D, causal, dtype, stream);
+  if (path == FwdPath::kD128) return launch_fwd_d128(a, causal, dtype, stream);
 #define FA_FWD_CASE(DD, CC, TT) \
   if (D == DD && causal == CC && dtype == TT::id) return launch_fwd_t<DD, kFwdQB, CC, TT>(a, stream);
   FA_FWD_CASE(64, false, Fp16)

@@ -121,6 +121,11 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o, c
                    void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
                    int causal, float scale, int dtype);
 
+// The kernel launch_fwd runs for B*H heads of N queries at head size D:
+// the key-split kernel (fa_fwd_short.hip), the 64-queries-per-wave kernel
+// (fa_fwd_d128.hip) or the 128-query kernel (fa_fwd.hip).
+enum class FwdPath { kShort, kD128, kTiled };
+FwdPath fwd_path(int64_t BH, int64_t N, int64_t D);
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 // The forward at D = 128 with 64 queries per wave (fa_fwd_d128.hip).
 hipError_t launch_fwd_d128(const FwdArgs& a, bool causal, int dtype, hipStream_t stream);

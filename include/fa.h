@@ -92,6 +92,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int causal, float scale, int dtype, void* stream);
 
 /*
+ * fa_fwd_kernel_name -- which forward kernel fa_fwd and fa_fwd_gqa run for
+ * a launch of this shape (host-only, no GPU work; for profiling and tests).
+ * All three compute the same online-softmax recurrence ("CUDA FlashAttention
+ * ...", §4) and differ only in how the work is cut, so results agree up to
+ * the order of floating-point additions:
+ *   "fwd_short_kernel" -- fewer than 256 tiles of 128 queries (B*H*ceil(N/128),
+ *       one per compute unit): 32 (D = 64) or 64 (D = 128) queries per
+ *       workgroup with the keys split over its four waves and the partial
+ *       states merged in LDS ("CUDA FlashAttention ...", §7, split along K);
+ *   "fwd_d128_kernel" -- D = 128 with at least 1024 tiles of 256 queries:
+ *       64 queries per wave, 256 per workgroup;
+ *   "fwd_kernel" -- otherwise: 32 queries per wave, 128 per workgroup.
+ * Returns a static string, "" for a shape fa_fwd would reject.
+ */
+const char* fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int causal);
+
+/*
  * fa_fwd_gqa -- fa_fwd with grouped K/V heads (GQA; H_kv = 1 is MQA).
  *   q, o : [B, H, N, D];  k, v : [B, H_kv, N, D];  lse : FP32 [B, H, N].
  *   H_kv must divide H; query head h of batch element b reads K/V head

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes",
                                     "fa_bwd_masked", "fa_bwd_masked_dropout", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
-                                    "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_masked_dropout", "fa_fwd_splitkv",
+                                    "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_kernel_name", "fa_fwd_masked", "fa_fwd_masked_dropout", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_masked", "fa_fwd_splitkv_num_splits",
                                     "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
                                     "fa_status_str"]
@@ -331,3 +331,17 @@ def test_bwd_noalloc_argument_errors_and_scratch_limit():
     assert fb.bwd_workspace_bytes(1, 1, 1 << 16, 128, 1, 0) > 32 << 20
     assert call(B=1, H=1, N=1 << 16, D=128) == 7
     assert "scratch" in fb.status_str(7)
+
+
+def test_fwd_kernel_name_follows_the_launch_size():
+    # no GPU work: the choice is made on the host from the shape alone
+    assert fb.fwd_kernel_name(1, 32, 8192, 128, 1) == "fwd_d128_kernel"   # 1024 tiles of 256 queries
+    assert fb.fwd_kernel_name(1, 16, 32768, 128, 1) == "fwd_d128_kernel"
+    assert fb.fwd_kernel_name(1, 32, 4096, 128, 1) == "fwd_kernel"        # 512 tiles of 256 queries
+    assert fb.fwd_kernel_name(1, 32, 4096, 64, 0) == "fwd_kernel"         # D = 64: never the D=128 kernel
+    assert fb.fwd_kernel_name(1, 32, 1024, 128, 1) == "fwd_kernel"        # 256 tiles of 128 queries
+    assert fb.fwd_kernel_name(1, 32, 512, 128, 1) == "fwd_short_kernel"   # 128 tiles of 128 queries
+    assert fb.fwd_kernel_name(1, 1, 256, 64, 0) == "fwd_short_kernel"
+    assert fb.fwd_kernel_name(1, 1, 16384, 128, 0) == "fwd_short_kernel"
+    assert fb.fwd_kernel_name(1, 1, 64, 96, 0) == ""                      # unsupported D
+    assert fb.fwd_kernel_name(0, 1, 64, 64, 0) == ""
