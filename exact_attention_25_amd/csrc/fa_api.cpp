@@ -295,7 +295,7 @@ const char* fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int c
   if (check_common(B, H, N, D, causal, 1.0f, FA_FP16) != FA_OK) return "";
   switch (fa::fwd_path(B * H, N, D)) {
     case fa::FwdPath::kShort:
-      return "fwd_short_kernel";
+      return fa::short_pipelined(N, D) ? "fwd_short_pipe_kernel" : "fwd_short_kernel";
     case fa::FwdPath::kD128:
       return "fwd_d128_kernel";
     default:

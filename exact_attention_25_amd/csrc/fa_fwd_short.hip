@@ -417,6 +417,396 @@ __global__ __launch_bounds__(kShortThreads, QB == 1 ? 2 : 1) void fwd_short_kern
   }
 }
 
+// Head size 128: the same cut (64 queries per workgroup, keys split over
+// the four waves, merge in LDS), with a wave's two 32-query blocks software-
+// pipelined against each other so that every MFMA has the other block's
+// vector work beside it.  A tile is four phases of 16 MFMA slots:
+//   C: scores of block 1 (tile t)       | exponentials, packs of block 0 (t)
+//   D: P V of block 0 (t)               | row max of block 1 (t), row sums
+//                                         of block 0, K fragments of t+1
+//   A: scores of block 0 (tile t+1)     | exponentials, packs of block 1 (t)
+//   B: P V of block 1 (t)               | row max of block 0 (t+1), row sums
+//                                         of block 1
+// each slot closed by a scheduling barrier.  Block 0's rescale decision for
+// tile t+1 is taken after B, block 1's for tile t after D, so each block's
+// reference is settled before its exponentials.  The V ring has two stages,
+// held in two LDS objects so that the compiler can tell the reads of one
+// stage from the copies in flight into the other; V of tile t is read in D
+// and B of its step and V of t+2 is copied into its stage after B.  On a
+// wave's last tile phase A computes scores from its own tile's K fragments
+// again and discards them (skipping them in a branch measured slower on long
+// walks); the pipeline pays off from about four tiles per wave, so shorter
+// sequences take fwd_short_kernel.
+
+// 16 wait states after the MFMAs that wrote one query block's two score
+// accumulators (or its four output accumulators), before vector access.
+__device__ __forceinline__ void block_scores_ready(f32x16 (&s)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+}
+__device__ __forceinline__ void block_o_ready(f32x16 (&o)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+}
+
+template <bool CAUSAL, class T>
+__global__ __launch_bounds__(kShortThreads, 1) void fwd_short_pipe_kernel(FwdArgs a) {
+  constexpr int D = 128, BN = kShortBN, WQ = 64;
+  constexpr int RC = D / 8, TC = BN * RC, LPW = TC / 64, NX = RC / 4, NC = D / 16, NDB = D / 32;
+  constexpr int NSL = 16;  // slots per phase: 2*NC score MFMAs = 4*NDB P V MFMAs per block
+  constexpr int PV = 2;    // V^T fragments read ahead of their MFMAs
+  static_assert(2 * NC == NSL && 4 * NDB == NSL, "phase length");
+
+  __shared__ u32x4 lds_vs0[kShortWaves][TC], lds_vs1[kShortWaves][TC];
+  __shared__ float lds_ml[kShortWaves][2][3][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ql = lane & 31, g = lane >> 5;
+
+  const int64_t N = a.N;
+  const int G = a.H / a.Hkv;
+  const int bh = head_of_slot(blockIdx.x % a.BH, a.BH, G);
+  const int rank = blockIdx.x / a.BH;
+  const int qt = CAUSAL ? (a.n_qtiles - 1 - rank) : rank;
+  const int q0 = qt * WQ;
+  const int64_t head = (int64_t)bh * N * D;
+  const int64_t kv_head = (int64_t)(bh / G) * N * D;
+  const uint16_t* __restrict__ Qh = a.q + head;
+  const uint16_t* __restrict__ Kh = a.k + kv_head;
+  const uint16_t* __restrict__ Vh = a.v + kv_head;
+
+  const int n_kt_all = (int)((N + BN - 1) / BN);
+  const int n_kt = CAUSAL ? min(n_kt_all, (q0 + WQ - 1) / BN + 1) : n_kt_all;
+
+  int vsrc[NX];
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    const int p = x * 64 + lane, r = p / RC;
+    vsrc[x] = (r * D + ((p % RC) ^ dual_xor<RC>(r)) * 8) * 2;
+  }
+  u32x4* const vst0 = lds_vs0[wave];
+  u32x4* const vst1 = lds_vs1[wave];
+
+  // K fragment f = kb*NC + c of lane (ql, g): K[64kt + 32kb + perm23(ql)][16c + 8g .. +8].
+  const int krow = perm23(ql);
+  u32x4 kf[2 * NC];
+  auto k_ptr = [&](int kt, int kb) __attribute__((always_inline)) {
+    return Kh + (int64_t)min(kt * BN + kb * 32 + krow, (int)N - 1) * D + g * 8;
+  };
+
+  u32x4 qa[2][NC], qv[2][NC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint16_t* row = Qh + (int64_t)min(q0 + 32 * qb + ql, (int)N - 1) * D + g * 8;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qv[qb][c] = *(const u32x4*)(row + c * 16);
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) asm volatile("s_nop 1" : "=a"(qa[qb][c]) : "0"(qv[qb][c]));
+
+  const int vj = lane & 15, vq = lane >> 4;
+  const int v_row0 = 8 * g + (vj >> 2);
+  const int v_col = 16 * (vq & 1) + 4 * (vj & 3);
+  const uint32_t v_off0 = dual_chunk<RC>(v_row0, v_col >> 3) * 16 + (v_col & 7) * 2;
+  const uint32_t v_off1 = dual_chunk<RC>(v_row0 + 4, v_col >> 3) * 16 + (v_col & 7) * 2;
+
+  f32x16 oacc[2][NDB];
+  float r_raw[2], mref[2], mlazy[2], m_use[2], mu[2], l_run[2], mx[2];
+  bool raw_mode[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[qb][i] = f32x16{};
+    r_raw[qb] = mref[qb] = mlazy[qb] = -INFINITY;
+    m_use[qb] = mu[qb] = l_run[qb] = 0.f;
+    raw_mode[qb] = false;
+  }
+  const float c2 = a.scale_log2;
+  f32x16 s[2][2];
+  u32x4 pf[2][4];
+  float mp[4], ls[4];
+
+  // Score MFMA i of block qb: accumulator kb = i % 2, chunk c = i / 2.
+  auto s_mfma = [&](int qb, int i) __attribute__((always_inline)) {
+    const int c = i >> 1, kb = i & 1;
+    if (c == 0)
+      mfma_s_first<T, true>(s[qb][kb], kf[kb * NC + c], qa[qb][c]);
+    else
+      mfma_s_acc<T, true>(s[qb][kb], kf[kb * NC + c], qa[qb][c]);
+  };
+  // K fragment of score slot i (issued one phase before that slot).
+  auto k_load = [&](int kt, int i) __attribute__((always_inline)) {
+    const int c = i >> 1, kb = i & 1;
+    kf[kb * NC + c] = *(const u32x4*)(k_ptr(kt, kb) + c * 16);
+  };
+  // V^T fragment of P V slot i: keys 16*(i/4) .., columns 32*(i%4) ..
+  auto v_read = [&](const u32x4* vb, int i) __attribute__((always_inline)) {
+    const char* base = (const char*)vb + (i >> 2) * 16 * RC * 16;
+    const int db = i & 3;
+    const u32x2 lo = lds_read_tr16(base + (v_off0 ^ (64 * db)));
+    const u32x2 hi = lds_read_tr16(base + (v_off1 ^ (64 * db)));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // Element pair p (0..15) of block qb in operand order: operand p/4,
+  // accumulator (p/4)/2, registers ((p/4)%2)*8 + 2*(p%4), +1.
+  auto exp_pair = [&](int qb, int p) __attribute__((always_inline)) {
+    const int o = p >> 2, kb = o >> 1, r = (o & 1) * 8 + 2 * (p & 3);
+    float e0 = fast_exp2(__builtin_fmaf(s[qb][kb][r], c2, -mu[qb]));
+    float e1 = fast_exp2(__builtin_fmaf(s[qb][kb][r + 1], c2, -mu[qb]));
+    // Computed in this slot: an empty volatile asm keeps IR-level passes
+    // from sinking the work past the slot's MFMA (volatile asm stays in order).
+    asm volatile("" : "+v"(e0), "+v"(e1));
+    s[qb][kb][r] = e0;
+    s[qb][kb][r + 1] = e1;
+  };
+  auto max_pair = [&](int qb, int p) __attribute__((always_inline)) {
+    const int o = p >> 2, kb = o >> 1, r = (o & 1) * 8 + 2 * (p & 3);
+    mp[p & 3] = fmaxf(mp[p & 3], fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
+    asm volatile("" : "+v"(mp[p & 3]));
+  };
+  // Row-sum share of slot i: dword i%4 of operand i/4 (fp16: the rounded
+  // probabilities that weight V; bf16: the FP32 ones).
+  auto sum_dw = [&](int qb, int i) __attribute__((always_inline)) {
+    const int o = i >> 2, w = i & 3;
+    if constexpr (T::id == Fp16::id) {
+      ls[o] = add_pair<T>(pf[qb][o][w], ls[o]);
+    } else {
+      const int kb = o >> 1, r = (o & 1) * 8 + 2 * w;
+      ls[o] += s[qb][kb][r];
+      ls[o] += s[qb][kb][r + 1];
+    }
+    asm volatile("" : "+v"(ls[o]));
+  };
+  auto mask_block = [&](int qb, int k0) __attribute__((always_inline)) {
+    if ((CAUSAL && k0 + BN - 1 > q0 + 32 * qb) || k0 + BN > N) {
+      const float ninf = -INFINITY;
+      const int lim = CAUSAL ? min(q0 + 32 * qb + ql, (int)N - 1) : (int)N - 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int t = lim - k0 - 32 * kb - 8 * g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          asm("v_cmp_gt_i32_e32 vcc, %1, %2\n\tv_cndmask_b32_e32 %0, %0, %3, vcc"
+              : "+v"(s[qb][kb][r])
+              : "i"(acc_row(r, 0)), "v"(t), "v"(ninf)
+              : "vcc");
+      }
+    }
+  };
+  // Reference of block qb for its current tile (see the tiled forward:
+  // lazy by kLazy in log2 units; raw mode for huge references); first: no
+  // tile of this block has been accumulated yet, so O and l are still zero.
+  auto decide = [&](int qb, bool first) __attribute__((always_inline)) {
+    if (wave_any(mx[qb] * c2 > mlazy[qb])) {
+      const float r_new = fmaxf(r_raw[qb], mx[qb]);
+      const float nm = r_new * c2;
+      const bool raw_new = wave_any(fabsf(nm) >= kShortFastLimit && nm != -INFINITY);
+      if (!first) {
+        const float lg = (raw_mode[qb] || raw_new) ? (r_raw[qb] - r_new) * c2 : mref[qb] - nm;
+        const float alpha = (r_raw[qb] == -INFINITY) ? 0.f : fast_exp2(lg);
+        block_o_ready(oacc[qb]);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) oacc[qb][i] *= alpha;
+      }
+      r_raw[qb] = r_new;
+      mref[qb] = nm;
+      mlazy[qb] = nm + kShortLazy;
+      m_use[qb] = (nm == -INFINITY) ? 0.f : nm;
+      raw_mode[qb] = raw_new;
+    }
+    mu[qb] = m_use[qb];
+    if (raw_mode[qb]) {
+      const float ru = (r_raw[qb] == -INFINITY) ? 0.f : r_raw[qb];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[qb][kb] -= ru;
+      mu[qb] = 0.f;
+    }
+  };
+  auto reset_max = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mp[c] = -INFINITY;
+  };
+  auto reset_sum = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ls[c] = 0.f;
+  };
+  auto fold_max = [&]() __attribute__((always_inline)) {
+    return xhalf_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+  };
+  auto fold_sum = [&]() __attribute__((always_inline)) { return (ls[0] + ls[1]) + (ls[2] + ls[3]); };
+
+  // Prologue: V of the first two tiles, K of the first; scores of block 0
+  // for the first tile, its max and reference.
+  int kt = wave;
+  if (kt < n_kt) {
+    copy_tile_wave<D, LPW, NX>(Vh + (int64_t)kt * BN * D, min(BN, (int)N - kt * BN), vsrc, vst0);
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) k_load(kt, i);
+    const int k1 = kt + kShortWaves;
+    if (k1 < n_kt) copy_tile_wave<D, LPW, NX>(Vh + (int64_t)k1 * BN * D, min(BN, (int)N - k1 * BN), vsrc, vst1);
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) s_mfma(0, i);
+    block_scores_ready(s[0]);
+    mask_block(0, kt * BN);
+    reset_max();
+#pragma unroll
+    for (int p = 0; p < NSL; ++p) max_pair(0, p);
+    mx[0] = fold_max();
+    decide(0, true);
+  }
+
+  for (int step = 0; kt < n_kt;) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      if (kt < n_kt) {
+        const bool more = kt + kShortWaves < n_kt;
+        const int kn = more ? kt + kShortWaves : kt;  // the last step re-reads K of its own tile
+        const u32x4* vb = par ? vst1 : vst0;
+        // C: scores of block 1 | exponentials and packs of block 0.
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+          s_mfma(1, i);
+          exp_pair(0, i);
+          if ((i & 3) == 3) {
+            pf[0][i >> 2] = pack8<T>(s[0][i >> 3], ((i >> 2) & 1) * 8);
+            asm volatile("" : "+v"(pf[0][i >> 2]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        block_scores_ready(s[1]);
+        mask_block(1, kt * BN);
+        reset_max();
+        reset_sum();
+        // D: P V of block 0 | max of block 1, row sums of block 0, K of the next tile.
+        u32x4 vqr[PV + 1];
+#pragma unroll
+        for (int i = 0; i < PV; ++i) vqr[i] = v_read(vb, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+          if (i + PV < NSL) vqr[(i + PV) % (PV + 1)] = v_read(vb, i + PV);
+          mfma_o<T, true>(oacc[0][i & 3], vqr[i % (PV + 1)], pf[0][i >> 2]);
+          max_pair(1, i);
+          sum_dw(0, i);
+          k_load(kn, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run[0] += fold_sum();
+        mx[1] = fold_max();
+        decide(1, step == 0);
+        // A: scores of block 0 for the next tile | exponentials and packs of block 1.
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+          s_mfma(0, i);
+          exp_pair(1, i);
+          if ((i & 3) == 3) {
+            pf[1][i >> 2] = pack8<T>(s[1][i >> 3], ((i >> 2) & 1) * 8);
+            asm volatile("" : "+v"(pf[1][i >> 2]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        block_scores_ready(s[0]);
+        if (more) mask_block(0, kn * BN);
+        reset_max();
+        reset_sum();
+        // B: P V of block 1 | max of block 0 (next tile), row sums of block 1.
+#pragma unroll
+        for (int i = 0; i < PV; ++i) vqr[i] = v_read(vb, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+          if (i + PV < NSL) vqr[(i + PV) % (PV + 1)] = v_read(vb, i + PV);
+          mfma_o<T, true>(oacc[1][i & 3], vqr[i % (PV + 1)], pf[1][i >> 2]);
+          max_pair(0, i);
+          sum_dw(1, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run[1] += fold_sum();
+        if (more) {
+          mx[0] = fold_max();
+          decide(0, false);
+        }
+        // V of the tile two steps ahead into this step's stage, once its reads have returned.
+        const int k2 = kt + 2 * kShortWaves;
+        if (k2 < n_kt) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          copy_tile_wave<D, LPW, NX>(Vh + (int64_t)k2 * BN * D, min(BN, (int)N - k2 * BN), vsrc,
+                                     par ? vst1 : vst0);
+        }
+        kt += kShortWaves;
+        ++step;
+      }
+    }
+  }
+  wait_vmem();
+  o_ready(oacc);
+
+  // Merge, as in fwd_short_kernel: every wave publishes its partial O (both
+  // stages of its ring hold the 32 KB) and per-row state; wave w finishes
+  // units w*8 .. w*8+7 (query block w/2, half of the head dimension).
+  {
+    float* const ob0 = (float*)vst0;
+    float* const ob1 = (float*)vst1;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float* const ob = qb ? ob1 : ob0;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *(f32x4*)(ob + ((db * 4 + rq) * 64 + lane) * 4) =
+              f32x4{oacc[qb][db][rq * 4], oacc[qb][db][rq * 4 + 1], oacc[qb][db][rq * 4 + 2],
+                    oacc[qb][db][rq * 4 + 3]};
+      lds_ml[wave][qb][0][lane] = r_raw[qb];
+      lds_ml[wave][qb][1][lane] =
+          (raw_mode[qb] || r_raw[qb] == -INFINITY) ? 0.f : __builtin_fmaf(r_raw[qb], c2, -mref[qb]);
+      lds_ml[wave][qb][2][lane] = xhalf_sum(l_run[qb]);
+    }
+  }
+  __syncthreads();
+
+  constexpr int UW = 2 * NDB * 4 / kShortWaves;  // 8 units per wave
+  const int mq = wave >> 1, u0 = (wave & 1) * UW;  // units of block mq: (db*4 + rq)
+  float R = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kShortWaves; ++w) R = fmaxf(R, lds_ml[w][mq][0][lane]);
+  float wt[kShortWaves], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kShortWaves; ++w) {
+    const float rw = lds_ml[w][mq][0][lane];
+    wt[w] = (rw == -INFINITY) ? 0.f : fast_exp2((rw - R) * c2 - lds_ml[w][mq][1][lane]);
+    L += wt[w] * lds_ml[w][mq][2][lane];
+  }
+  f32x4 part[kShortWaves][UW];
+#pragma unroll
+  for (int w = 0; w < kShortWaves; ++w) {
+    const float* obw = (const float*)(mq ? lds_vs1[w] : lds_vs0[w]);
+#pragma unroll
+    for (int j = 0; j < UW; ++j) part[w][j] = *(const f32x4*)(obw + ((u0 + j) * 64 + lane) * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int my_q = q0 + 32 * mq + ql;
+  if (my_q < N) {
+    const float inv = 1.f / L;
+    uint16_t* Orow = a.o + head + (int64_t)my_q * D;
+#pragma unroll
+    for (int j = 0; j < UW; ++j) {
+      f32x4 acc = wt[0] * part[0][j];
+#pragma unroll
+      for (int w = 1; w < kShortWaves; ++w) acc += wt[w] * part[w][j];
+      const int u = u0 + j, db = u >> 2, rq = u & 3;
+      u32x2 o2;
+      o2[0] = pack2<T>(acc[0] * inv, acc[1] * inv);
+      o2[1] = pack2<T>(acc[2] * inv, acc[3] * inv);
+      *(u32x2*)(Orow + db * 32 + rq * 8 + g * 4) = o2;
+    }
+    if (u0 == 0 && g == 0) a.lse[(int64_t)bh * N + my_q] = (R * c2 + __log2f(L)) * kLn2;
+  }
+}
+
 // D = 64 takes one query block per wave (measured faster for the smallest
 // grids, where two workgroups share a CU); D = 128 two.
 template <int D, bool CAUSAL, class T>
@@ -424,8 +814,13 @@ hipError_t launch_short_t(FwdArgs a, hipStream_t stream) {
   constexpr int QB = D == 64 ? 1 : 2;
   a.n_qtiles = (int)((a.N + 32 * QB - 1) / (32 * QB));
   const int64_t n_wg = (int64_t)a.BH * a.n_qtiles;
-  hipLaunchKernelGGL((fwd_short_kernel<D, QB, CAUSAL, T>), dim3((unsigned)n_wg), dim3(kShortThreads), 0, stream,
-                     a);
+  // D = 128 from N = 1024 (a wave walks at least four tiles when causal):
+  // the pipelined kernel; measured slower than the plain one below that.
+  if (short_pipelined(a.N, D))
+    hipLaunchKernelGGL((fwd_short_pipe_kernel<CAUSAL, T>), dim3((unsigned)n_wg), dim3(kShortThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_short_kernel<D, QB, CAUSAL, T>), dim3((unsigned)n_wg), dim3(kShortThreads), 0, stream,
+                       a);
   return hipGetLastError();
 }
 

@@ -126,6 +126,9 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o, c
 // (fa_fwd_d128.hip) or the 128-query kernel (fa_fwd.hip).
 enum class FwdPath { kShort, kD128, kTiled };
 FwdPath fwd_path(int64_t BH, int64_t N, int64_t D);
+// Within the key-split path: D = 128 from N = 1024 on runs the software-
+// pipelined variant (fwd_short_pipe_kernel), shorter or D = 64 the plain one.
+inline bool short_pipelined(int64_t N, int64_t D) { return D == 128 && N >= 1024; }
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream);
 // The forward at D = 128 with 64 queries per wave (fa_fwd_d128.hip).
 hipError_t launch_fwd_d128(const FwdArgs& a, bool causal, int dtype, hipStream_t stream);

@@ -101,6 +101,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *       one per compute unit): 32 (D = 64) or 64 (D = 128) queries per
  *       workgroup with the keys split over its four waves and the partial
  *       states merged in LDS ("CUDA FlashAttention ...", §7, split along K);
+ *   "fwd_short_pipe_kernel" -- the same split at D = 128 and N >= 1024, with
+ *       a wave's two query blocks software-pipelined against each other;
  *   "fwd_d128_kernel" -- D = 128 with at least 1024 tiles of 256 queries:
  *       64 queries per wave, 256 per workgroup;
  *   "fwd_kernel" -- otherwise: 32 queries per wave, 128 per workgroup.

@@ -342,6 +342,8 @@ def test_fwd_kernel_name_follows_the_launch_size():
     assert fb.fwd_kernel_name(1, 32, 1024, 128, 1) == "fwd_kernel"        # 256 tiles of 128 queries
     assert fb.fwd_kernel_name(1, 32, 512, 128, 1) == "fwd_short_kernel"   # 128 tiles of 128 queries
     assert fb.fwd_kernel_name(1, 1, 256, 64, 0) == "fwd_short_kernel"
-    assert fb.fwd_kernel_name(1, 1, 16384, 128, 0) == "fwd_short_kernel"
+    assert fb.fwd_kernel_name(1, 1, 16384, 128, 0) == "fwd_short_pipe_kernel"  # pipelined from N = 1024
+    assert fb.fwd_kernel_name(1, 16, 1024, 128, 1) == "fwd_short_pipe_kernel"
+    assert fb.fwd_kernel_name(1, 8, 1000, 128, 1) == "fwd_short_kernel"
     assert fb.fwd_kernel_name(1, 1, 64, 96, 0) == ""                      # unsupported D
     assert fb.fwd_kernel_name(0, 1, 64, 64, 0) == ""
