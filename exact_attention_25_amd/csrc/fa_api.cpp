@@ -293,7 +293,7 @@ size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D
 
 const char* fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int causal) {
   if (check_common(B, H, N, D, causal, 1.0f, FA_FP16) != FA_OK) return "";
-  switch (fa::fwd_path(B * H, N, D)) {
+  switch (fa::fwd_path(B * H, N, D, causal != 0)) {
     case fa::FwdPath::kShort:
       return fa::short_pipelined(N, D) ? "fwd_short_pipe_kernel" : "fwd_short_kernel";
     case fa::FwdPath::kD128:

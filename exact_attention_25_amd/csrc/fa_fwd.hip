@@ -715,17 +715,24 @@ hipError_t launch_fwd_split_t(FwdArgs a, hipStream_t stream) {
 // key-split forward of fa_fwd_short.hip; at D = 128 with at least
 // kD128From 256-query tiles, the 64-queries-per-wave kernel; otherwise this
 // file's 128-query kernel (thresholds from measured sweeps over N and H).
+// A causal launch of exactly one tile per compute unit with long keys
+// (N >= kShortCausalFrom) also takes the key-split forward: there the
+// 128-query kernel's heaviest workgroup walks all N/64 key tiles alone at
+// the end (measured: one head N = 32768 0.36 vs 0.49 ms, two heads N = 16384
+// 0.19 vs 0.25 ms).
 constexpr int64_t kShortBelow = 256;
+constexpr int64_t kShortCausalFrom = 8192;
 constexpr int64_t kD128From = 1024;
 
-FwdPath fwd_path(int64_t BH, int64_t N, int64_t D) {
-  if (BH * ((N + 127) / 128) < kShortBelow) return FwdPath::kShort;
+FwdPath fwd_path(int64_t BH, int64_t N, int64_t D, bool causal) {
+  const int64_t tiles = BH * ((N + 127) / 128);
+  if (tiles < kShortBelow || (causal && tiles == kShortBelow && N >= kShortCausalFrom)) return FwdPath::kShort;
   if (D == 128 && BH * ((N + 255) / 256) >= kD128From) return FwdPath::kD128;
   return FwdPath::kTiled;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, int dtype, hipStream_t stream) {
-  const FwdPath path = fwd_path(a.BH, a.N, D);
+  const FwdPath path = fwd_path(a.BH, a.N, D, causal);
   if (path == FwdPath::kShort) return launch_fwd_short(a, D, causal, dtype, stream);
   if (path == FwdPath::kD128) return launch_fwd_d128(a, causal, dtype, stream);
 #define FA_FWD_CASE(DD, CC, TT) \

@@ -125,7 +125,7 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o, c
 // the key-split kernel (fa_fwd_short.hip), the 64-queries-per-wave kernel
 // (fa_fwd_d128.hip) or the 128-query kernel (fa_fwd.hip).
 enum class FwdPath { kShort, kD128, kTiled };
-FwdPath fwd_path(int64_t BH, int64_t N, int64_t D);
+FwdPath fwd_path(int64_t BH, int64_t N, int64_t D, bool causal);
 // Within the key-split path: D = 128 from N = 1024 on runs the software-
 // pipelined variant (fwd_short_pipe_kernel), shorter or D = 64 the plain one.
 inline bool short_pipelined(int64_t N, int64_t D) { return D == 128 && N >= 1024; }

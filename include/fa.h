@@ -98,7 +98,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * ...", §4) and differ only in how the work is cut, so results agree up to
  * the order of floating-point additions:
  *   "fwd_short_kernel" -- fewer than 256 tiles of 128 queries (B*H*ceil(N/128),
- *       one per compute unit): 32 (D = 64) or 64 (D = 128) queries per
+ *       one per compute unit), or causal with exactly 256 and N >= 8192
+ *       (there one workgroup would walk every key tile alone at the end):
+ *       32 (D = 64) or 64 (D = 128) queries per
  *       workgroup with the keys split over its four waves and the partial
  *       states merged in LDS ("CUDA FlashAttention ...", §7, split along K);
  *   "fwd_short_pipe_kernel" -- the same split at D = 128 and N >= 1024, with

@@ -340,6 +340,9 @@ def test_fwd_kernel_name_follows_the_launch_size():
     assert fb.fwd_kernel_name(1, 32, 4096, 128, 1) == "fwd_kernel"        # 512 tiles of 256 queries
     assert fb.fwd_kernel_name(1, 32, 4096, 64, 0) == "fwd_kernel"         # D = 64: never the D=128 kernel
     assert fb.fwd_kernel_name(1, 32, 1024, 128, 1) == "fwd_kernel"        # 256 tiles of 128 queries
+    assert fb.fwd_kernel_name(1, 1, 32768, 128, 1) == "fwd_short_pipe_kernel"  # 256 tiles, causal, long keys
+    assert fb.fwd_kernel_name(1, 1, 32768, 128, 0) == "fwd_kernel"        # the same, not causal
+    assert fb.fwd_kernel_name(1, 2, 32768, 128, 1) == "fwd_kernel"        # 512 tiles
     assert fb.fwd_kernel_name(1, 32, 512, 128, 1) == "fwd_short_kernel"   # 128 tiles of 128 queries
     assert fb.fwd_kernel_name(1, 1, 256, 64, 0) == "fwd_short_kernel"
     assert fb.fwd_kernel_name(1, 1, 16384, 128, 0) == "fwd_short_pipe_kernel"  # pipelined from N = 1024

@@ -65,6 +65,24 @@ WORKLOADS = [workloads.SMALL, workloads.NONCAUSAL_D64, *workloads.CAUSAL_D128.va
              workloads.FWDBWD_D64, workloads.LONG_BF16]
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fwd_causal_long_keys_one_tile_per_cu(dtype):
+    """Causal, 256 tiles of 128 queries and N >= 8192: the key-split forward
+    (its heaviest wave walks 64 of the 256 key tiles).  256 sampled query
+    rows of each head -- the first and last 64, every 64th, the rest random --
+    against the oracle."""
+    B, H, N, D = 1, 2, 16384, 128
+    assert fa.fwd_kernel_name(B, H, N, D, 1) == "fwd_short_pipe_kernel"
+    say("fwd causal long keys B=%d H=%d N=%d %s" % (B, H, N, dtype))
+    inp = make_inputs(B, H, N, D, dtype, seed=1700)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = run_fwd(inp, dtype, True, scale)
+    rows = _sample_rows(N, 256, np.random.default_rng(1701))
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], True, scale, rows=rows)
+    assert_fwd_close(to_host(o)[:, :, rows], to_host(lse)[:, :, rows], o_ref, lse_ref, dtype,
+                     "N=%d, %d rows per head" % (N, rows.size))
+
+
 @pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
 def test_fwd_workload(w):
     """The whole output of every head against the oracle (the golden-reference
