@@ -143,9 +143,9 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
   auto copy_part = [&](const uint16_t* base, int tile, int src0, u32x4* dst, int p) __attribute__((always_inline)) {
     const int valid = tile < n_kt ? min(kBN, (int)N - tile * kBN) : 0;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + (int64_t)tile * kBN * kD, valid * kD * 2);
-    int wofs = wave * 64;
+    int wofs = wave * 64 * 16;  // bytes: the destination is then one scalar add
     asm volatile("" : "+s"(wofs));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + wofs + p * kNT), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)((char*)dst + wofs + p * kNT * 16), 16,
                                              src0 * 2, p * kNT * 16, 0, 0);
   };
   auto copy_k = [&](int tile, int buf, int p) __attribute__((always_inline)) {
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
     scores_ready(s_nxt);
 
     // ---- phase B ----
-    float lsum[2] = {0.f, 0.f}, mn[2] = {-INFINITY, -INFINITY};
+    float lsum[2] = {0.f, 0.f}, lsum2[2] = {0.f, 0.f}, mn[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < 2 * NV; ++i) {
       const int qb = i & 1, v = i >> 1, t = v / (kD / 32), db = v % (kD / 32);
@@ -364,7 +364,15 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
       {  // row sum of dword i/2 of block qb (packed at least eight slots ago)
         const int d = i >> 1;
         if constexpr (T::id == Fp16::id) {
-          lsum[qb] = add_pair<T>(pf[qb][d >> 2][d & 3], lsum[qb]);
+          // The two halves of the dword go to two FP32 sums, so that the two
+          // v_fma_mix of a slot do not wait for each other.  (Adding dword
+          // pairs as fp16 first saves instructions but its extra rounding
+          // was measured to cost accuracy.)
+          asm("v_fma_mix_f32 %0, %2, 1.0, %0 op_sel_hi:[1,0,0]\n\t"
+              "v_fma_mix_f32 %1, %2, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+              : "+v"(lsum[qb]), "+v"(lsum2[qb])
+              : "v"(pf[qb][d >> 2][d & 3]));
+          asm volatile("" : "+v"(lsum2[qb]));
         } else {
           const int lo = ((d >> 2) & 1) * 8 + 2 * (d & 3);
           lsum[qb] += s[qb][d >> 3][lo];
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      l_run[qb] += lsum[qb];
+      l_run[qb] += lsum[qb] + lsum2[qb];
       mx[qb] = xhalf_max(mn[qb]);
     }
     // The row max of tile j+1 was taken beside the MFMAs (with no branch
