@@ -165,8 +165,19 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // which is how partial tiles are read.  The descriptor lives in scalar
 // registers when `base` and `bytes` are wave-uniform.  Word 3 (0x00020000)
 // is the gfx9 family's data-format field for untyped 32-bit loads.
+//
+// A buffer resource lives in scalar registers, so `base` and `bytes` must be
+// the same in every lane (every caller passes one tile of its workgroup).
+// They are read from the first lane: where the compiler cannot prove them
+// uniform it would otherwise wrap each load in a loop over the distinct
+// values of the lanes (measured in the backward's dK/dV pass: sixteen such
+// loops per two query tiles).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // Direct copy of one 64-row tile of a row-major [rows, D] tensor by NT
