@@ -500,10 +500,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 || !DROP) ? 2 : 1) void dkdv_ker
         for (int r = 0; r < 16; ++r) kbits |= ((wq[r] >> l32) & 1u) << r;
       }
       const float ks = DROP ? a.drop.keep_scale : 1.f;
+      // Causal mask on the raw scores, only on blocks that meet the diagonal
+      // (a uniform branch; as a select on every block it cost a quarter of
+      // the loop's instructions at D = 64).
+      if (__builtin_expect(diag, 0)) {
+        asm volatile("");  // keeps the branch
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (my_k > qb0 + acc_row(r, g)) s[r] = -INFINITY;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(s[r], c2, -lse_r[r]));
-        if (diag && my_k > qb0 + acc_row(r, g)) p = 0.f;
         if constexpr (DROP) {
           const bool keep = (kbits >> r) & 1u;
           s[r] = keep ? p * ks : 0.f;                         // dropped, scaled P for dV
