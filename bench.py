@@ -24,12 +24,12 @@ bounded sample of the same workload.
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters can be calibrated against a
 kernel whose HBM traffic is known.
 --mode fwd-only / bwd-only launch just that pass K times (for profiling).
---splits S times fa_fwd_splitkv with S key splits instead of fa_fwd (S = auto:
+--splits S times the split-K/V forward (fa_fwd_ex, fa_options.num_splits = S) instead of fa_fwd (S = auto:
 the count fa_fwd_splitkv_num_splits picks for the workload).
 --kv-heads G gives K and V only G heads (grouped-query attention).
---dropout P times fa_fwd_dropout / fa_bwd_dropout (seed 1234, offset 0);
-with --mask too, fa_fwd_masked_dropout / fa_bwd_masked_dropout.
---mask KIND times fa_fwd_masked / fa_bwd_masked with a seeded key-padding
+--dropout P times fa_fwd_ex / fa_bwd_ex with dropout (seed 1234, offset 0);
+with --mask too, with both options.
+--mask KIND times fa_fwd_ex / fa_bwd_ex with a seeded key-padding
 mask (lengths / random / blocks / all); TFLOP/s then count only the visible
 (query, key) pairs, and the one-off tile-table build is reported apart.
 """
@@ -69,14 +69,14 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--mode", default="bench", choices=["bench", "copy", "fwd-only", "bwd-only"])
     p.add_argument("--splits", default="0",
-                   help="time fa_fwd_splitkv with this many key splits (split pass + merge) instead of fa_fwd; "
+                   help="time the split-K/V forward with this many key splits (split pass + merge) instead of fa_fwd; "
                         "'auto': the count fa_fwd_splitkv_num_splits picks")
     p.add_argument("--dropout", type=float, default=0.0,
-                   help="time fa_fwd_dropout / fa_bwd_dropout with this dropout probability (seed 1234, offset 0)")
+                   help="time fa_fwd_ex / fa_bwd_ex with dropout of this probability (seed 1234, offset 0)")
     p.add_argument("--kv-heads", type=int, default=0,
                    help="grouped heads: K and V get this many heads (must divide H); 0 = H")
     p.add_argument("--mask", default=None, choices=["lengths", "random", "blocks", "all"],
-                   help="time fa_fwd_masked / fa_bwd_masked with a seeded key-padding mask of this kind; "
+                   help="time fa_fwd_ex / fa_bwd_ex with a seeded key-padding mask of this kind; "
                         "FLOPs then count only visible (query, key) pairs")
     return p.parse_args()
 
@@ -234,7 +234,7 @@ def main():
         torch.cuda.synchronize()
         mask_ms = (time.perf_counter() - t0) / 10 * 1e3
 
-    if args.dropout:  # with --mask as well: fa_fwd_masked_dropout
+    if args.dropout:  # with --mask as well: both options
         def run_fwd():
             fa.fwd_dropout(q, k, v, args.dropout, 1234, 0, causal=w.causal, scale=w.scale, out=o, lse=lse,
                            tiles=tiles)
@@ -242,8 +242,9 @@ def main():
         def run_fwd():
             fa.fwd_masked(q, k, v, tiles, causal=w.causal, scale=w.scale, out=o, lse=lse)
     elif args.splits > 0:
-        split_ws = torch.empty(max(256, fa.fwd_splitkv_workspace_bytes(
-            w.B, w.H, w.N, w.D, w.causal, 0 if w.dtype == "fp16" else 1, args.splits)), dtype=torch.uint8, device=dev)
+        split_ws = torch.empty(max(256, fa.fwd_ex_workspace_bytes(
+            w.B, w.H, w.N, w.D, w.causal, 0 if w.dtype == "fp16" else 1, fa.options(num_splits=args.splits))),
+            dtype=torch.uint8, device=dev)
 
         def run_fwd():
             fa.fwd_splitkv(q, k, v, args.splits, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=split_ws)
@@ -251,8 +252,8 @@ def main():
         def run_fwd():
             fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
-    ws = torch.empty(max(256, fa.bwd_gqa_workspace_bytes(w.B, w.H, hkv, w.N, w.D, w.causal,
-                                                         0 if w.dtype == "fp16" else 1)),
+    ws = torch.empty(max(256, fa.bwd_ex_workspace_bytes(w.B, w.H, w.N, w.D, w.causal, 0 if w.dtype == "fp16" else 1,
+                                                        fa.options(h_kv=hkv))),
                      dtype=torch.uint8, device=dev)
 
     def run_bwd():

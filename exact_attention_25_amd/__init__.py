@@ -9,10 +9,10 @@ fallback implementation.
 """
 
 _BINDING_NAMES = ("fwd", "bwd", "fwd_splitkv", "fwd_masked", "bwd_masked", "mask_tiles", "fwd_dropout",
-                  "bwd_dropout", "dropout_mask", "fa_fwd_dropout", "fa_bwd_dropout", "fa_dropout_mask", "fa_fwd_masked_dropout", "fa_bwd_masked_dropout", "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_masked",
-                  "fa_fwd", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_splitkv", "fa_fwd_masked", "fa_bwd_masked", "fa_mask_tiles",
-                  "fa_mask_tiles_bytes", "bwd_workspace_bytes", "bwd_gqa_workspace_bytes", "fwd_splitkv_workspace_bytes", "splitkv_num_splits", "fwd_kernel_name", "status_str",
-                  "load_library", "FaError", "library_path")
+                  "bwd_dropout", "dropout_mask", "fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_noalloc",
+                  "fa_dropout_mask", "fa_mask_tiles", "fa_mask_tiles_bytes", "options", "FaOptions",
+                  "bwd_workspace_bytes", "fwd_ex_workspace_bytes", "bwd_ex_workspace_bytes", "splitkv_num_splits",
+                  "fwd_kernel_name", "status_str", "load_library", "FaError", "library_path")
 
 
 def __getattr__(name):

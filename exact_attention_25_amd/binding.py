@@ -28,6 +28,26 @@ class FaError(RuntimeError):
         super().__init__("%s%s" % (what + ": " if what else "", status_str(status)))
 
 
+class FaOptions(ctypes.Structure):
+    """struct fa_options of include/fa.h (the optional features of a call)."""
+    _fields_ = [("h_kv", ctypes.c_int64), ("mask_tiles", ctypes.c_void_p), ("dropout", ctypes.c_int),
+                ("dropout_p", ctypes.c_float), ("dropout_seed", ctypes.c_uint64),
+                ("dropout_offset", ctypes.c_uint64), ("num_splits", ctypes.c_int)]
+
+
+def options(h_kv=0, tiles=0, dropout=None, num_splits=0):
+    """FaOptions from plain values: tiles is a device address (0: no mask),
+    dropout is None or (p, seed, offset)."""
+    o = FaOptions()
+    o.h_kv = int(h_kv)
+    o.mask_tiles = int(tiles) or None
+    if dropout is not None:
+        p, seed, offset = dropout
+        o.dropout, o.dropout_p, o.dropout_seed, o.dropout_offset = 1, float(p), int(seed), int(offset)
+    o.num_splits = int(num_splits)
+    return o
+
+
 _lib = None
 
 
@@ -51,61 +71,28 @@ def load_library():
     lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                            ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
     lib.fa_bwd.restype = ctypes.c_int
-    lib.fa_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                               ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp]
-    lib.fa_fwd_gqa.restype = ctypes.c_int
-    lib.fa_bwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                               ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
-    lib.fa_bwd_gqa.restype = ctypes.c_int
-    lib.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
-                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
-    lib.fa_fwd_splitkv.restype = ctypes.c_int
-    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
-    lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_splitkv_num_splits.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
     lib.fa_fwd_splitkv_num_splits.restype = ctypes.c_int
     lib.fa_fwd_kernel_name.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
     lib.fa_fwd_kernel_name.restype = ctypes.c_char_p
     lib.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.fa_bwd_gqa_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
-    lib.fa_bwd_gqa_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_mask_tiles_bytes.argtypes = [_i64, _i64]
     lib.fa_mask_tiles_bytes.restype = ctypes.c_size_t
     lib.fa_mask_tiles.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_size_t, _vp]
     lib.fa_mask_tiles.restype = ctypes.c_int
-    lib.fa_fwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, _vp]
-    lib.fa_fwd_masked.restype = ctypes.c_int
-    lib.fa_bwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, _vp, ctypes.c_size_t, _vp]
-    lib.fa_bwd_masked.restype = ctypes.c_int
+    _opt = ctypes.POINTER(FaOptions)
+    lib.fa_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                              ctypes.c_int, _opt, _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_ex.restype = ctypes.c_int
+    lib.fa_bwd_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                              ctypes.c_float, ctypes.c_int, _opt, _vp, ctypes.c_size_t, _vp]
+    lib.fa_bwd_ex.restype = ctypes.c_int
+    lib.fa_fwd_ex_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _opt]
+    lib.fa_fwd_ex_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_ex_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _opt]
+    lib.fa_bwd_ex_workspace_bytes.restype = ctypes.c_size_t
     _u64 = ctypes.c_uint64
-    lib.fa_fwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
-                                   ctypes.c_float, ctypes.c_int, ctypes.c_float, _u64, _u64, _vp]
-    lib.fa_fwd_dropout.restype = ctypes.c_int
-    lib.fa_bwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float, _u64, _u64,
-                                   _vp, ctypes.c_size_t, _vp]
-    lib.fa_bwd_dropout.restype = ctypes.c_int
-    lib.fa_fwd_splitkv_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
-                                           ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, _u64, _u64,
-                                           _vp, ctypes.c_size_t, _vp]
-    lib.fa_fwd_splitkv_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
-                                       ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
-    lib.fa_fwd_splitkv_gqa.restype = ctypes.c_int
-    lib.fa_fwd_splitkv_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
-                                          ctypes.c_float, ctypes.c_int, _vp, ctypes.c_int, ctypes.c_float, _u64, _u64,
-                                          _vp, ctypes.c_size_t, _vp]
-    lib.fa_fwd_splitkv_masked.restype = ctypes.c_int
-    lib.fa_fwd_splitkv_dropout.restype = ctypes.c_int
-    lib.fa_fwd_masked_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
-                                          ctypes.c_float, ctypes.c_int, _vp, ctypes.c_float, _u64, _u64, _vp]
-    lib.fa_fwd_masked_dropout.restype = ctypes.c_int
-    lib.fa_bwd_masked_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
-                                          _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_float,
-                                          _u64, _u64, _vp, ctypes.c_size_t, _vp]
-    lib.fa_bwd_masked_dropout.restype = ctypes.c_int
     lib.fa_dropout_mask.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_float, _u64, _u64, _vp]
     lib.fa_dropout_mask.restype = ctypes.c_int
     lib.fa_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -137,25 +124,29 @@ def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale,
                                          float(scale), int(dtype), stream)
 
 
-def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, stream):
-    return load_library().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale), int(dtype),
-                                     stream)
+def fa_fwd_ex(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, opt, workspace, workspace_bytes, stream):
+    """fa_fwd_ex; opt is an FaOptions or None."""
+    return load_library().fa_fwd_ex(q, k, v, o, lse, B, H, N, D, int(causal), float(scale), int(dtype),
+                                    ctypes.byref(opt) if opt is not None else None, workspace, workspace_bytes,
+                                    stream)
 
 
-def fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype,
-               workspace, workspace_bytes, stream):
-    return load_library().fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
-                                     float(scale), int(dtype), workspace, workspace_bytes, stream)
+def fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, opt, workspace,
+              workspace_bytes, stream):
+    """fa_bwd_ex; opt is an FaOptions or None."""
+    return load_library().fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, int(causal), float(scale),
+                                    int(dtype), ctypes.byref(opt) if opt is not None else None, workspace,
+                                    workspace_bytes, stream)
 
 
-def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, num_splits, workspace,
-                   workspace_bytes, stream):
-    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, D, int(causal), float(scale), int(dtype),
-                                         int(num_splits), workspace, workspace_bytes, stream)
+def fwd_ex_workspace_bytes(B, H, N, D, causal, dtype, opt=None):
+    return int(load_library().fa_fwd_ex_workspace_bytes(B, H, N, D, int(causal), int(dtype),
+                                                        ctypes.byref(opt) if opt is not None else None))
 
 
-def fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits):
-    return int(load_library().fa_fwd_splitkv_workspace_bytes(B, H, N, D, int(causal), int(dtype), int(num_splits)))
+def bwd_ex_workspace_bytes(B, H, N, D, causal, dtype, opt=None):
+    return int(load_library().fa_bwd_ex_workspace_bytes(B, H, N, D, int(causal), int(dtype),
+                                                        ctypes.byref(opt) if opt is not None else None))
 
 
 def splitkv_num_splits(B, H, N, D, causal):
@@ -172,55 +163,6 @@ def bwd_workspace_bytes(B, H, N, D, causal, dtype):
     return int(load_library().fa_bwd_workspace_bytes(B, H, N, D, int(causal), int(dtype)))
 
 
-def bwd_gqa_workspace_bytes(B, H, H_kv, N, D, causal, dtype):
-    return int(load_library().fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, D, int(causal), int(dtype)))
-
-
-def fa_fwd_dropout(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, dropout_p, seed, offset, stream):
-    return load_library().fa_fwd_dropout(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale), int(dtype),
-                                         float(dropout_p), int(seed), int(offset), stream)
-
-
-def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, dropout_p, seed,
-                   offset, workspace, workspace_bytes, stream):
-    return load_library().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
-                                         float(scale), int(dtype), float(dropout_p), int(seed), int(offset),
-                                         workspace, workspace_bytes, stream)
-
-
-def fa_fwd_splitkv_dropout(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, dropout_p, seed,
-                           offset, workspace, workspace_bytes, stream):
-    return load_library().fa_fwd_splitkv_dropout(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
-                                                 int(dtype), int(num_splits), float(dropout_p), int(seed),
-                                                 int(offset), workspace, workspace_bytes, stream)
-
-
-def fa_fwd_splitkv_masked(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, tiles, num_splits, dropout_p,
-                          seed, offset, workspace, workspace_bytes, stream):
-    return load_library().fa_fwd_splitkv_masked(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
-                                                int(dtype), tiles, int(num_splits), float(dropout_p), int(seed),
-                                                int(offset), workspace, workspace_bytes, stream)
-
-
-def fa_fwd_splitkv_gqa(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, workspace,
-                       workspace_bytes, stream):
-    return load_library().fa_fwd_splitkv_gqa(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
-                                             int(dtype), int(num_splits), workspace, workspace_bytes, stream)
-
-
-def fa_fwd_masked_dropout(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, tiles, dropout_p, seed, offset,
-                          stream):
-    return load_library().fa_fwd_masked_dropout(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale),
-                                                int(dtype), tiles, float(dropout_p), int(seed), int(offset), stream)
-
-
-def fa_bwd_masked_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, tiles,
-                          dropout_p, seed, offset, workspace, workspace_bytes, stream):
-    return load_library().fa_bwd_masked_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
-                                                float(scale), int(dtype), tiles, float(dropout_p), int(seed),
-                                                int(offset), workspace, workspace_bytes, stream)
-
-
 def fa_dropout_mask(keep, B, H, N, dropout_p, seed, offset, stream):
     return load_library().fa_dropout_mask(keep, B, H, N, float(dropout_p), int(seed), int(offset), stream)
 
@@ -231,17 +173,6 @@ def fa_mask_tiles_bytes(B, N):
 
 def fa_mask_tiles(key_mask, B, N, tiles, tiles_bytes, stream):
     return load_library().fa_mask_tiles(key_mask, B, N, tiles, tiles_bytes, stream)
-
-
-def fa_fwd_masked(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, tiles, stream):
-    return load_library().fa_fwd_masked(q, k, v, o, lse, B, H, H_kv, N, D, int(causal), float(scale), int(dtype),
-                                        tiles, stream)
-
-
-def fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, tiles,
-                  workspace, workspace_bytes, stream):
-    return load_library().fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, int(causal),
-                                        float(scale), int(dtype), tiles, workspace, workspace_bytes, stream)
 
 
 # ---- torch-tensor convenience wrappers ----
@@ -284,12 +215,8 @@ def _kv_heads(q, k):
     return hkv
 
 
-def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
-    """O, LSE = attention forward of fp16/bf16 device tensors q [B, H, N, D]
-    and k, v [B, H_kv, N, D] (H_kv = H, or a divisor of H for grouped heads).
-
-    Returns (o, lse) with o like q and lse float32 [B, H, N].
-    """
+def _fwd(q, k, v, causal, scale, out, lse, opt, workspace, what):
+    """Checks, allocations and one fa_fwd / fa_fwd_ex call; opt None = plain."""
     import torch
     hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
@@ -303,82 +230,28 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check({"out": out}, q.shape, q.dtype, q.device)
     _check({"lse": lse}, (B, H, N), torch.float32, q.device)
-    if hkv == H:
-        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, H, N, D, causal, scale, _dtype_code(q), _stream_handle(q.device))
-    else:
-        st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        B, H, hkv, N, D, causal, scale, _dtype_code(q), _stream_handle(q.device))
-    if st != FA_OK:
-        raise FaError(st, "fa_fwd" if hkv == H else "fa_fwd_gqa")
-    return out, lse
-
-
-def fwd_splitkv(q, k, v, num_splits=None, causal=False, scale=None, out=None, lse=None, workspace=None,
-                dropout=None, tiles=None):
-    """fa_fwd_splitkv: the forward with keys split into num_splits ranges and
-    the partial states merged (num_splits=None: fa_fwd_splitkv_num_splits's
-    choice for the shape).  k, v may have fewer heads (grouped:
-    fa_fwd_splitkv_gqa).  dropout=(p, seed, offset): fa_fwd_splitkv_dropout,
-    the same result as fwd_dropout.  tiles (from mask_tiles()):
-    fa_fwd_splitkv_masked, with or without dropout.  Returns (o, lse) like fwd."""
-    import torch
-    hkv = _kv_heads(q, k)
-    B, H, N, D = q.shape
-    _check({"q": q}, q.shape, q.dtype, q.device)
-    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
-    if num_splits is None:
-        num_splits = splitkv_num_splits(B, H, N, D, causal)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     code = _dtype_code(q)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    _check({"out": out}, q.shape, q.dtype, q.device)
-    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
-    need = fwd_splitkv_workspace_bytes(B, H, N, D, causal, code, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if tiles is not None:
-        if tiles.numel() < fa_mask_tiles_bytes(B, N):
-            raise ValueError("tile table too small for B=%d N=%d" % (B, N))
-        p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
-        st = fa_fwd_splitkv_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
-                                   hkv, N, D, causal, scale, code, tiles.data_ptr(), num_splits, p, seed, offset,
-                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                   _stream_handle(q.device))
-        if st != FA_OK:
-            raise FaError(st, "fa_fwd_splitkv_masked")
-        return out, lse
-    if dropout is not None:
-        p, seed, offset = dropout
-        st = fa_fwd_splitkv_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
-                                    hkv, N, D, causal, scale, code, num_splits, p, seed, offset,
-                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                    _stream_handle(q.device))
-        if st != FA_OK:
-            raise FaError(st, "fa_fwd_splitkv_dropout")
-        return out, lse
     if hkv != H:
-        st = fa_fwd_splitkv_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, hkv,
-                                N, D, causal, scale, code, num_splits, workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream_handle(q.device))
-        if st != FA_OK:
-            raise FaError(st, "fa_fwd_splitkv_gqa")
-        return out, lse
-    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D,
-                        causal, scale, code, num_splits, workspace.data_ptr(),
-                        workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+        opt = opt if opt is not None else options()
+        opt.h_kv = hkv
+    if opt is None:
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, D, causal, scale, code, _stream_handle(q.device))
+    else:
+        need = fwd_ex_workspace_bytes(B, H, N, D, causal, code, opt)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) if workspace is not None \
+            else (None, 0)
+        st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, H, N, D, causal, scale, code, opt, ws, wsb, _stream_handle(q.device))
     if st != FA_OK:
-        raise FaError(st, "fa_fwd_splitkv")
+        raise FaError(st, what if opt is not None else "fa_fwd")
     return out, lse
 
 
-def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
-    """dQ, dK, dV of the attention forward, by recomputation (dK, dV shaped
-    like k, v: grouped heads get the sum over their query heads)."""
+def _bwd(q, k, v, o, lse, dout, causal, scale, opt, workspace, what):
+    """Checks, allocations and one fa_bwd / fa_bwd_ex call; opt None = plain."""
     import torch
     hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
@@ -388,21 +261,58 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     code = _dtype_code(q)
-    need = bwd_gqa_workspace_bytes(B, H, hkv, N, D, causal, code)
+    if hkv != H:
+        opt = opt if opt is not None else options()
+        opt.h_kv = hkv
+    need = bwd_ex_workspace_bytes(B, H, N, D, causal, code, opt)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
-    tail = (N, D, causal, scale, code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            _stream_handle(q.device))
-    if hkv == H:
-        st = fa_bwd(*args, B, H, *tail)
-    else:
-        st = fa_bwd_gqa(*args, B, H, hkv, *tail)
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, causal, scale, code)
+    wsa = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    st = fa_bwd(*args, *wsa) if opt is None else fa_bwd_ex(*args, opt, *wsa)
     if st != FA_OK:
-        raise FaError(st, "fa_bwd" if hkv == H else "fa_bwd_gqa")
+        raise FaError(st, what if opt is not None else "fa_bwd")
     return dq, dk, dv
+
+
+def _tiles_addr(tiles, B, N):
+    if tiles is None:
+        return 0
+    if tiles.numel() < fa_mask_tiles_bytes(B, N):
+        raise ValueError("tile table too small for B=%d N=%d" % (B, N))
+    return tiles.data_ptr()
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """O, LSE = attention forward of fp16/bf16 device tensors q [B, H, N, D]
+    and k, v [B, H_kv, N, D] (H_kv = H, or a divisor of H for grouped heads:
+    fa_fwd_ex with fa_options.h_kv).
+
+    Returns (o, lse) with o like q and lse float32 [B, H, N].
+    """
+    return _fwd(q, k, v, causal, scale, out, lse, None, None, "fa_fwd_ex")
+
+
+def fwd_splitkv(q, k, v, num_splits=None, causal=False, scale=None, out=None, lse=None, workspace=None,
+                dropout=None, tiles=None):
+    """The forward with keys split into num_splits ranges and the partial
+    states merged (fa_fwd_ex with fa_options.num_splits; None: the count of
+    fa_fwd_splitkv_num_splits for the shape).  k, v may have fewer heads
+    (grouped).  dropout=(p, seed, offset): the same result as fwd_dropout.
+    tiles (from mask_tiles()): with a key-padding mask.  Returns (o, lse)."""
+    B, H, N, D = q.shape
+    if num_splits is None:
+        num_splits = splitkv_num_splits(B, H, N, D, causal)
+    opt = options(tiles=_tiles_addr(tiles, B, N), dropout=dropout, num_splits=num_splits)
+    return _fwd(q, k, v, causal, scale, out, lse, opt, workspace, "fa_fwd_ex (split-K/V)")
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
+    """dQ, dK, dV of the attention forward, by recomputation (dK, dV shaped
+    like k, v: grouped heads get the sum over their query heads)."""
+    return _bwd(q, k, v, o, lse, dout, causal, scale, None, workspace, "fa_bwd_ex")
 
 
 def mask_tiles(key_mask):
@@ -424,124 +334,37 @@ def mask_tiles(key_mask):
 
 
 def fwd_masked(q, k, v, tiles, causal=False, scale=None, out=None, lse=None):
-    """fa_fwd_masked with the tile table from mask_tiles().  Returns (o, lse);
+    """The forward with a key-padding mask given by its tile table from
+    mask_tiles() (fa_fwd_ex with fa_options.mask_tiles).  Returns (o, lse);
     rows with no visible key get o = 0 and lse = -inf."""
-    import torch
-    hkv = _kv_heads(q, k)
     B, H, N, D = q.shape
-    _check({"q": q}, q.shape, q.dtype, q.device)
-    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    _check({"out": out}, q.shape, q.dtype, q.device)
-    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
-    if tiles.numel() < fa_mask_tiles_bytes(B, N):
-        raise ValueError("tile table too small for B=%d N=%d" % (B, N))
-    st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                       B, H, hkv, N, D, causal, scale, _dtype_code(q), tiles.data_ptr(), _stream_handle(q.device))
-    if st != FA_OK:
-        raise FaError(st, "fa_fwd_masked")
-    return out, lse
+    opt = options(tiles=_tiles_addr(tiles, B, N))
+    return _fwd(q, k, v, causal, scale, out, lse, opt, None, "fa_fwd_ex (mask)")
 
 
 def bwd_masked(q, k, v, o, lse, dout, tiles, causal=False, scale=None, workspace=None):
-    """fa_bwd_masked: gradients of fwd_masked with the same tile table."""
-    import torch
-    hkv = _kv_heads(q, k)
+    """Gradients of fwd_masked with the same tile table."""
     B, H, N, D = q.shape
-    _check({"q": q, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
-    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
-    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if tiles.numel() < fa_mask_tiles_bytes(B, N):
-        raise ValueError("tile table too small for B=%d N=%d" % (B, N))
-    code = _dtype_code(q)
-    need = bwd_gqa_workspace_bytes(B, H, hkv, N, D, causal, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, hkv, N, D, causal, scale, code,
-                       tiles.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                       _stream_handle(q.device))
-    if st != FA_OK:
-        raise FaError(st, "fa_bwd_masked")
-    return dq, dk, dv
+    opt = options(tiles=_tiles_addr(tiles, B, N))
+    return _bwd(q, k, v, o, lse, dout, causal, scale, opt, workspace, "fa_bwd_ex (mask)")
 
 
 def fwd_dropout(q, k, v, dropout_p, seed, offset=0, causal=False, scale=None, out=None, lse=None, tiles=None):
-    """fa_fwd_dropout: forward with attention dropout regenerated from
-    (seed, offset).  k, v may have fewer heads (grouped).  With tiles (from
-    mask_tiles()), fa_fwd_masked_dropout.  Returns (o, lse)."""
-    import torch
-    hkv = _kv_heads(q, k)
+    """The forward with attention dropout regenerated from (seed, offset)
+    (fa_fwd_ex with fa_options.dropout).  k, v may have fewer heads
+    (grouped); with tiles (from mask_tiles()) also a key-padding mask.
+    Returns (o, lse)."""
     B, H, N, D = q.shape
-    _check({"q": q}, q.shape, q.dtype, q.device)
-    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    _check({"out": out}, q.shape, q.dtype, q.device)
-    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
-    if tiles is not None:
-        if tiles.numel() < fa_mask_tiles_bytes(B, N):
-            raise ValueError("tile table too small for B=%d N=%d" % (B, N))
-        st = fa_fwd_masked_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
-                                   hkv, N, D, causal, scale, _dtype_code(q), tiles.data_ptr(), dropout_p, seed,
-                                   offset, _stream_handle(q.device))
-        if st != FA_OK:
-            raise FaError(st, "fa_fwd_masked_dropout")
-        return out, lse
-    st = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, hkv, N, D,
-                        causal, scale, _dtype_code(q), dropout_p, seed, offset, _stream_handle(q.device))
-    if st != FA_OK:
-        raise FaError(st, "fa_fwd_dropout")
-    return out, lse
+    opt = options(tiles=_tiles_addr(tiles, B, N), dropout=(dropout_p, seed, offset))
+    return _fwd(q, k, v, causal, scale, out, lse, opt, None, "fa_fwd_ex (dropout)")
 
 
 def bwd_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, causal=False, scale=None, workspace=None,
                 tiles=None):
-    """fa_bwd_dropout: gradients of fwd_dropout with the same (p, seed, offset)
-    (and the same tile table: fa_bwd_masked_dropout)."""
-    import torch
-    hkv = _kv_heads(q, k)
+    """Gradients of fwd_dropout with the same (p, seed, offset) and tile table."""
     B, H, N, D = q.shape
-    _check({"q": q, "o": o, "dout": dout}, q.shape, q.dtype, q.device)
-    _check({"k": k, "v": v}, (B, hkv, N, D), q.dtype, q.device)
-    _check({"lse": lse}, (B, H, N), torch.float32, q.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    code = _dtype_code(q)
-    need = bwd_gqa_workspace_bytes(B, H, hkv, N, D, causal, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    if tiles is not None:
-        if tiles.numel() < fa_mask_tiles_bytes(B, N):
-            raise ValueError("tile table too small for B=%d N=%d" % (B, N))
-        st = fa_bwd_masked_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                   dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, hkv, N, D,
-                                   causal, scale, code, tiles.data_ptr(), dropout_p, seed, offset,
-                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                   _stream_handle(q.device))
-        if st != FA_OK:
-            raise FaError(st, "fa_bwd_masked_dropout")
-        return dq, dk, dv
-    st = fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, hkv, N, D, causal, scale, code,
-                        dropout_p, seed, offset, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                        _stream_handle(q.device))
-    if st != FA_OK:
-        raise FaError(st, "fa_bwd_dropout")
-    return dq, dk, dv
+    opt = options(tiles=_tiles_addr(tiles, B, N), dropout=(dropout_p, seed, offset))
+    return _bwd(q, k, v, o, lse, dout, causal, scale, opt, workspace, "fa_bwd_ex (dropout)")
 
 
 def dropout_mask(B, H, N, dropout_p, seed, offset=0, device="cuda"):

@@ -214,6 +214,8 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o, c
 
 namespace {
 
+size_t splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t D, int splits);
+
 // The split-K/V forward for H_kv K/V heads, with dropout when drop_p >= 0 and
 // a key-padding mask when tiles is not NULL.
 int splitkv_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
@@ -225,7 +227,7 @@ int splitkv_common(const void* q, const void* k, const void* v, void* o, float* 
   if (tiles && !aligned16(tiles)) return FA_ERR_ALIGN;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
   if (B * H * ((N + 63) / 64) > kMaxWorkgroups / num_splits) return FA_ERR_SHAPE;
-  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, N, D, causal, dtype, num_splits);
+  const size_t need = splitkv_workspace(B, H, N, D, num_splits);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
@@ -244,6 +246,42 @@ int splitkv_common(const void* q, const void* k, const void* v, void* o, float* 
                           : fa::launch_fwd_splitkv_masked(a, d, c, dtype, s));
   }
   return status_of(drop ? fa::launch_fwd_splitkv_dropout(a, d, c, dtype, s) : fa::launch_fwd_splitkv(a, d, c, dtype, s));
+}
+
+// The options of an _ex call, checked (opt == NULL: the defaults).  The
+// backward ignores num_splits.
+struct Options {
+  int64_t h_kv;
+  const void* tiles;
+  bool drop;
+  float p;
+  uint64_t seed, offset;
+  int splits;
+};
+int64_t option_h_kv(const fa_options* opt, int64_t H) { return (opt && opt->h_kv != 0) ? opt->h_kv : H; }
+int read_options(const fa_options* opt, int64_t H, bool forward, Options* o) {
+  *o = Options{H, nullptr, false, 0.f, 0, 0, 0};
+  if (!opt) return FA_OK;
+  o->h_kv = option_h_kv(opt, H);
+  if (check_heads(H, o->h_kv) != FA_OK) return FA_ERR_SHAPE;
+  if (opt->dropout != 0 && opt->dropout != 1) return FA_ERR_UNSUPPORTED;
+  o->drop = opt->dropout == 1;
+  o->p = opt->dropout_p;
+  o->seed = opt->dropout_seed;
+  o->offset = opt->dropout_offset;
+  if (o->drop && !(o->p >= 0.f && o->p < 1.f)) return FA_ERR_UNSUPPORTED;
+  if (forward) {
+    if (opt->num_splits < 0 || opt->num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+    o->splits = opt->num_splits;
+  }
+  o->tiles = opt->mask_tiles;
+  if (o->tiles && !aligned16(o->tiles)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+size_t splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t D, int splits) {
+  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(splits);
+  return align256(rows * sizeof(float)) + align256(rows * static_cast<size_t>(D) * sizeof(float));
 }
 
 }  // namespace
@@ -270,25 +308,40 @@ const char* fa_status_str(int status) {
 
 // ---- forward ---------------------------------------------------------------
 
-int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-               int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, void* stream) {
-  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  const fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
-  return status_of(fa::launch_fwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
-}
-
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
            int64_t D, int causal, float scale, int dtype, void* stream) {
-  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype, stream);
+  return fa_fwd_ex(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, nullptr, nullptr, 0, stream);
 }
 
-size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
-                                      int num_splits) {
+size_t fa_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                                 const fa_options* opt) {
   if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK) return 0;
-  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
-  const size_t rows = static_cast<size_t>(B * H * N) * static_cast<size_t>(num_splits);
-  return align256(rows * sizeof(float)) + align256(rows * static_cast<size_t>(D) * sizeof(float));
+  Options op;
+  if (read_options(opt, H, true, &op) != FA_OK) return 0;
+  return op.splits > 0 ? splitkv_workspace(B, H, N, D, op.splits) : 0;
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+              int64_t D, int causal, float scale, int dtype, const fa_options* opt, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int st = check_fwd(q, k, v, o, lse, B, H, option_h_kv(opt, H), N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  Options op;
+  st = read_options(opt, H, true, &op);
+  if (st != FA_OK) return st;
+  if (op.splits > 0)
+    return splitkv_common(q, k, v, o, lse, B, H, op.h_kv, N, D, causal, scale, dtype, op.splits,
+                          op.drop ? op.p : -1.f, op.seed, op.offset, op.tiles, workspace, workspace_bytes, stream);
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, op.h_kv, N, scale);
+  if (op.drop && !dropout_args(op.p, op.seed, op.offset, &a.drop)) return FA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = static_cast<int>(D);
+  const bool c = causal != 0;
+  if (op.tiles) {
+    a.mask = mask_tiles_view(op.tiles, B, N);
+    return status_of(op.drop ? fa::launch_fwd_masked_dropout(a, d, c, dtype, s) : fa::launch_fwd_masked(a, d, c, dtype, s));
+  }
+  return status_of(op.drop ? fa::launch_fwd_dropout(a, d, c, dtype, s) : fa::launch_fwd(a, d, c, dtype, s));
 }
 
 const char* fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int causal) {
@@ -314,22 +367,6 @@ int fa_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t D, int ca
   return s;
 }
 
-int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                   int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-  return splitkv_common(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype, num_splits, -1.f, 0, 0, nullptr,
-                        workspace, workspace_bytes, stream);
-}
-
-int fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                       int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits,
-                       void* workspace, size_t workspace_bytes, void* stream) {
-  return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, -1.f, 0, 0, nullptr,
-                        workspace, workspace_bytes, stream);
-}
-
-// ---- key-padding masks -----------------------------------------------------
-
 size_t fa_mask_tiles_bytes(int64_t B, int64_t N) {
   if (B <= 0 || N <= 0 || N > kMaxN) return 0;
   const int64_t T = (N + 63) / 64;
@@ -349,19 +386,6 @@ int fa_mask_tiles(const uint8_t* key_mask, int64_t B, int64_t N, void* tiles, si
                                          const_cast<int*>(m.list), static_cast<hipStream_t>(stream)));
 }
 
-int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                  int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
-                  void* stream) {
-  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  if (!tiles) return FA_ERR_NULL;
-  if (!aligned16(tiles)) return FA_ERR_ALIGN;
-  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
-  a.mask = mask_tiles_view(tiles, B, N);
-  return status_of(
-      fa::launch_fwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
-}
-
 // ---- backward --------------------------------------------------------------
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype) {
@@ -369,118 +393,41 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int ca
   return bwd_workspace_layout(B, H, H, N, D);
 }
 
-size_t fa_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, int causal,
-                                  int dtype) {
-  if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK || check_heads(H, H_kv) != FA_OK) return 0;
-  return bwd_workspace_layout(B, H, H_kv, N, D);
-}
-
-int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-               void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D, int causal,
-               float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
-                           workspace_bytes);
-  if (st != FA_OK) return st;
-  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, scale, workspace);
-  return status_of(fa::launch_bwd(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
-}
-
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, D, causal, scale, dtype, workspace,
-                    workspace_bytes, stream);
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, scale, dtype, nullptr, workspace,
+                   workspace_bytes, stream);
 }
 
-int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                  void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                  int causal, float scale, int dtype, const void* tiles, void* workspace, size_t workspace_bytes,
-                  void* stream) {
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
-                           workspace_bytes);
+size_t fa_bwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                                 const fa_options* opt) {
+  if (check_common(B, H, N, D, causal, 1.0f, dtype) != FA_OK) return 0;
+  Options op;
+  if (read_options(opt, H, false, &op) != FA_OK) return 0;
+  return bwd_workspace_layout(B, H, op.h_kv, N, D);
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
+              int dtype, const fa_options* opt, void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t h_kv = option_h_kv(opt, H);
+  int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, h_kv, N, D, causal, scale, dtype, workspace,
+                     workspace_bytes);
   if (st != FA_OK) return st;
-  if (!tiles) return FA_ERR_NULL;
-  if (!aligned16(tiles)) return FA_ERR_ALIGN;
-  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, scale, workspace);
-  a.mask = mask_tiles_view(tiles, B, N);
-  return status_of(
-      fa::launch_bwd_masked(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
-}
-
-// ---- dropout ---------------------------------------------------------------
-
-int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                   int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, float dropout_p,
-                   uint64_t seed, uint64_t offset, void* stream) {
-  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
+  Options op;
+  st = read_options(opt, H, false, &op);
   if (st != FA_OK) return st;
-  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
-  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
-  return status_of(
-      fa::launch_fwd_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
-}
-
-int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                   void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                   int causal, float scale, int dtype, float dropout_p, uint64_t seed, uint64_t offset,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
-                           workspace_bytes);
-  if (st != FA_OK) return st;
-  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, scale, workspace);
-  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
-  return status_of(
-      fa::launch_bwd_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
-}
-
-int fa_fwd_splitkv_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                           int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, int num_splits,
-                           float dropout_p, uint64_t seed, uint64_t offset, void* workspace, size_t workspace_bytes,
-                           void* stream) {
-  if (!(dropout_p >= 0.f)) return FA_ERR_UNSUPPORTED;  // NaN or negative; the rest as for the other dropout calls
-  return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits, dropout_p, seed, offset,
-                        nullptr, workspace, workspace_bytes, stream);
-}
-
-int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                          int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
-                          int num_splits, float dropout_p, uint64_t seed, uint64_t offset, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  if (!tiles) return FA_ERR_NULL;
-  if (!(dropout_p >= 0.f)) return FA_ERR_UNSUPPORTED;
-  return splitkv_common(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype, num_splits,
-                        dropout_p > 0.f ? dropout_p : -1.f, seed, offset, tiles, workspace, workspace_bytes, stream);
-}
-
-int fa_fwd_masked_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                          int64_t H_kv, int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
-                          float dropout_p, uint64_t seed, uint64_t offset, void* stream) {
-  const int st = check_fwd(q, k, v, o, lse, B, H, H_kv, N, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  if (!tiles) return FA_ERR_NULL;
-  if (!aligned16(tiles)) return FA_ERR_ALIGN;
-  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, H_kv, N, scale);
-  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
-  a.mask = mask_tiles_view(tiles, B, N);
-  return status_of(
-      fa::launch_fwd_masked_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
-}
-
-int fa_bwd_masked_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                          const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv,
-                          int64_t N, int64_t D, int causal, float scale, int dtype, const void* tiles,
-                          float dropout_p, uint64_t seed, uint64_t offset, void* workspace, size_t workspace_bytes,
-                          void* stream) {
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, causal, scale, dtype, workspace,
-                           workspace_bytes);
-  if (st != FA_OK) return st;
-  if (!tiles) return FA_ERR_NULL;
-  if (!aligned16(tiles)) return FA_ERR_ALIGN;
-  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, D, scale, workspace);
-  if (!dropout_args(dropout_p, seed, offset, &a.drop)) return FA_ERR_UNSUPPORTED;
-  a.mask = mask_tiles_view(tiles, B, N);
-  return status_of(
-      fa::launch_bwd_masked_dropout(a, static_cast<int>(D), causal != 0, dtype, static_cast<hipStream_t>(stream)));
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, op.h_kv, N, D, scale, workspace);
+  if (op.drop && !dropout_args(op.p, op.seed, op.offset, &a.drop)) return FA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = static_cast<int>(D);
+  const bool c = causal != 0;
+  if (op.tiles) {
+    a.mask = mask_tiles_view(op.tiles, B, N);
+    return status_of(op.drop ? fa::launch_bwd_masked_dropout(a, d, c, dtype, s) : fa::launch_bwd_masked(a, d, c, dtype, s));
+  }
+  return status_of(op.drop ? fa::launch_bwd_dropout(a, d, c, dtype, s) : fa::launch_bwd(a, d, c, dtype, s));
 }
 
 int fa_dropout_mask(uint8_t* keep, int64_t B, int64_t H, int64_t N, float dropout_p, uint64_t seed, uint64_t offset,

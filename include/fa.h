@@ -92,9 +92,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int causal, float scale, int dtype, void* stream);
 
 /*
- * fa_fwd_kernel_name -- which forward kernel fa_fwd and fa_fwd_gqa run for
- * a launch of this shape (host-only, no GPU work; for profiling and tests).
- * All three compute the same online-softmax recurrence ("CUDA FlashAttention
+ * fa_fwd_kernel_name -- which forward kernel fa_fwd (and fa_fwd_ex with no
+ * mask, dropout or split) runs for a launch of this shape (host-only, no GPU work; for profiling and tests).
+ * All four compute the same online-softmax recurrence ("CUDA FlashAttention
  * ...", §4) and differ only in how the work is cut, so results agree up to
  * the order of floating-point additions:
  *   "fwd_short_kernel" -- fewer than 256 tiles of 128 queries (B*H*ceil(N/128),
@@ -113,80 +113,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 const char* fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int causal);
 
 /*
- * fa_fwd_gqa -- fa_fwd with grouped K/V heads (GQA; H_kv = 1 is MQA).
- *   q, o : [B, H, N, D];  k, v : [B, H_kv, N, D];  lse : FP32 [B, H, N].
- *   H_kv must divide H; query head h of batch element b reads K/V head
- *   h / (H / H_kv) of b in place -- no copy of K or V is made ("CUDA
- *   FlashAttention ...", §7: query heads map onto a shared K/V head, and
- *   their reuse is planned with the workgroup schedule: the workgroups of
- *   one group are numbered onto the same XCD when B*H_kv is a multiple of 8).
- * fa_fwd(...) is fa_fwd_gqa(..., H, H, ...).  Errors as for fa_fwd, plus
- * FA_ERR_SHAPE when H_kv < 1 or H_kv does not divide H.
- */
-int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
-               int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-               int causal, float scale, int dtype, void* stream);
-
-/*
- * fa_fwd_splitkv_workspace_bytes -- bytes of device workspace fa_fwd_splitkv
- * needs for num_splits partial states: an FP32 LSE and an FP32 D-vector per
- * query row and split, i.e. num_splits*B*H*N*(D+1)*4 (each part rounded up
- * to 256).  Returns 0 for arguments fa_fwd_splitkv would reject.
- */
-size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
-                                      int causal, int dtype, int num_splits);
-
-/*
- * fa_fwd_splitkv_num_splits -- a split count for fa_fwd_splitkv on this
- * shape ("CUDA FlashAttention ...", §7: split along K when N is long and
- * B*H is small, so that there are enough workgroups).  The forward runs one
- * workgroup per 128 queries, W = B*H*ceil(N/128) of them; the count doubles,
- * from 1, while W*S < 512 (two workgroups per compute unit), each of the S
- * ranges would keep at least 2048 keys after the doubling, and S < 16.
- * Returns 1 when splitting would not pay (for example B=1 H=32 N=8192), and
- * 0 for a shape fa_fwd would reject.  Host-only: no GPU work.
- */
-int fa_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t D, int causal);
-
-/*
- * fa_fwd_splitkv -- the same result as fa_fwd, with the keys split into
- * num_splits contiguous ranges of whole 64-key tiles ("CUDA FlashAttention
- * ...", §7: for long N and small B*H, split along K; every part yields a
- * local (m, l, o) and the parts are combined with the merge formula of §4).
- *   Pass 1: one workgroup per (query tile, split) writes, for each query row,
- *           the split's LSE_s and its output O_s normalised within the split
- *           (FP32, in `workspace`); a row with no visible key in the split
- *           gets LSE_s = -inf.
- *   Pass 2: per row, LSE = m + ln sum_s exp(LSE_s - m) with m = max_s LSE_s,
- *           and O = sum_s exp(LSE_s - LSE) O_s, rounded to `dtype` (RNE).
- *   num_splits : 1 .. 64 (more splits than key tiles leaves some empty).
- *   workspace  : caller-owned device memory of at least
- *                fa_fwd_splitkv_workspace_bytes(...) bytes, 16-byte aligned;
- *                contents on entry ignored, on return unspecified.
- *   Other arguments, layouts and errors as for fa_fwd; additionally
- *   FA_ERR_WORKSPACE for a missing or short workspace and
- *   FA_ERR_UNSUPPORTED for num_splits outside 1 .. 64.
- */
-int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int64_t B, int64_t H, int64_t N, int64_t D,
-                   int causal, float scale, int dtype, int num_splits,
-                   void* workspace, size_t workspace_bytes, void* stream);
-
-/* fa_fwd_splitkv_gqa -- fa_fwd_splitkv for k, v with H_kv K/V heads (H_kv
- * divides H; query head h reads K/V head h / (H / H_kv), as in fa_fwd_gqa).
- * Workspace as for fa_fwd_splitkv (it holds per-query-head states); errors
- * as for fa_fwd_splitkv plus FA_ERR_SHAPE for an H_kv that does not divide H. */
-int fa_fwd_splitkv_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                       int causal, float scale, int dtype, int num_splits,
-                       void* workspace, size_t workspace_bytes, void* stream);
-
-/*
  * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one FP32
  * value per query row for Delta_i = rowsum(dO_i * O_i), i.e. 4*B*H*N, rounded
  * up to 256; plus, when B*H*ceil(N/128) is too small to fill the GPU (few
  * heads of a long sequence), FP32 partial dK and dV as described for
- * fa_bwd_gqa_workspace_bytes.  Returns 0 for arguments fa_bwd would reject.
+ * fa_bwd_ex_workspace_bytes.  Returns 0 for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
                               int causal, int dtype);
@@ -242,36 +173,6 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    int causal, float scale, int dtype, void* stream);
 
 /*
- * fa_bwd_gqa_workspace_bytes -- bytes of device workspace fa_bwd_gqa and
- * fa_bwd_masked need: Delta (4*B*H*N), plus, when the dK/dV pass splits the
- * query positions of each K/V head (its G query heads' query tiles) into
- * P > 1 parts (few K/V heads: the pass would otherwise have too few
- * workgroups to fill the GPU; P is at most the larger of G and the number of
- * 8-tile groups of query tiles), FP32 partial dK and dV of 4*P*B*H_kv*N*D bytes each; sections
- * rounded up to 256.  Returns 0 for arguments fa_bwd_gqa would reject.
- * Equals fa_bwd_workspace_bytes when H_kv = H.
- */
-size_t fa_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                                  int causal, int dtype);
-
-/*
- * fa_bwd_gqa -- fa_bwd for a forward computed by fa_fwd_gqa.
- *   dk, dv : [B, H_kv, N, D]; every other tensor as in fa_fwd_gqa / fa_bwd.
- * The gradient of a shared K/V head is the sum over the H / H_kv query heads
- * that read it.  One workgroup per 128 keys walks its part of the query
- * tiles of the group's heads, accumulating in FP32 registers; with several
- * parts a reduce kernel adds the parts' FP32 sums in a fixed order, so the
- * result is bitwise reproducible either way.
- * Workspace: fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, D, ...).
- */
-int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
-               const float* lse, const void* dout,
-               void* dq, void* dk, void* dv,
-               int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-               int causal, float scale, int dtype,
-               void* workspace, size_t workspace_bytes, void* stream);
-
-/*
  * Key-padding masks (padded variable-length batches).
  *
  * A key-padding mask key_mask[B][N] (bytes, nonzero = visible) hides keys
@@ -284,8 +185,8 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
  * Block-level flags ("FlashAttention dataflow and engineering validation on
  * MI50", §4.3: on 64-wide waves the padding test belongs to the block loop,
  * once per block, not to every element): fa_mask_tiles compresses the byte
- * mask once into a tile table, which fa_fwd_masked and fa_bwd_masked read
- * instead of the mask.  They visit only tiles with a visible key, and test
+ * mask once into a tile table, which fa_fwd_ex and fa_bwd_ex read (through
+ * fa_options.mask_tiles) instead of the mask.  They visit only tiles with a visible key, and test
  * elements only in tiles that are partly visible.
  *
  * Tile table (T = ceil(N/64); offsets from `tiles`, each section starting
@@ -316,31 +217,6 @@ size_t fa_mask_tiles_bytes(int64_t B, int64_t N);
 int fa_mask_tiles(const uint8_t* key_mask, int64_t B, int64_t N, void* tiles, size_t tiles_bytes, void* stream);
 
 /*
- * fa_fwd_masked -- fa_fwd_gqa with a key-padding mask given by its tile
- * table (built by fa_mask_tiles for the same B and N; its contents are
- * trusted).  Arguments, layouts and errors otherwise as for fa_fwd_gqa
- * (pass H_kv = H for plain multi-head attention); FA_ERR_NULL for a NULL
- * table.
- */
-int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
-                  int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                  int causal, float scale, int dtype, const void* tiles, void* stream);
-
-/*
- * fa_bwd_masked -- fa_bwd_gqa for a forward computed by fa_fwd_masked with
- * the same tile table.  Hidden keys get dK = dV = 0 exactly; rows without a
- * visible key (LSE = -inf) get dQ = 0.  Arguments, workspace
- * (fa_bwd_gqa_workspace_bytes) and errors as for fa_bwd_gqa; FA_ERR_NULL for
- * a NULL table.
- */
-int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
-                  const float* lse, const void* dout,
-                  void* dq, void* dk, void* dv,
-                  int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                  int causal, float scale, int dtype, const void* tiles,
-                  void* workspace, size_t workspace_bytes, void* stream);
-
-/*
  * Attention dropout, regenerated instead of stored ("Why FlashAttention does
  * not need to store the attention matrix", §05: the kernel keeps only the
  * Philox seed and offset, and the backward pass rebuilds the same mask;
@@ -357,75 +233,8 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
  * dropout_p must lie in [0, 1) (else FA_ERR_UNSUPPORTED); p = 0 keeps all.
  */
 
-/* fa_fwd_dropout -- fa_fwd_gqa with dropout (p, seed, offset). */
-int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                   int causal, float scale, int dtype,
-                   float dropout_p, uint64_t seed, uint64_t offset, void* stream);
-
-/* fa_bwd_dropout -- fa_bwd_gqa for a forward computed by fa_fwd_dropout with
- * the same (p, seed, offset); workspace: fa_bwd_gqa_workspace_bytes. */
-int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
-                   const float* lse, const void* dout,
-                   void* dq, void* dk, void* dv,
-                   int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                   int causal, float scale, int dtype,
-                   float dropout_p, uint64_t seed, uint64_t offset,
-                   void* workspace, size_t workspace_bytes, void* stream);
-
 /*
- * fa_fwd_masked_dropout, fa_bwd_masked_dropout -- the two calls above with a
- * key-padding mask given by its tile table, as in fa_fwd_masked /
- * fa_bwd_masked: hidden keys get P = 0 before dropout applies, the keep
- * mask is the same (p, seed, offset) stream, and a row with no visible key
- * gets O = 0, LSE = -inf, dQ = 0.  Errors as for the dropout calls, plus
- * FA_ERR_NULL / FA_ERR_ALIGN for the table.
- */
-int fa_fwd_masked_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
-                          int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                          int causal, float scale, int dtype, const void* tiles,
-                          float dropout_p, uint64_t seed, uint64_t offset, void* stream);
-int fa_bwd_masked_dropout(const void* q, const void* k, const void* v, const void* o,
-                          const float* lse, const void* dout,
-                          void* dq, void* dk, void* dv,
-                          int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                          int causal, float scale, int dtype, const void* tiles,
-                          float dropout_p, uint64_t seed, uint64_t offset,
-                          void* workspace, size_t workspace_bytes, void* stream);
-
-/*
- * fa_fwd_splitkv_dropout -- fa_fwd_dropout computed as fa_fwd_splitkv does
- * (keys split into num_splits ranges, FP32 partial states, merge): each
- * split drops and scales its probabilities, its partial LSE is that of the
- * undropped ones, so the merge weights are unchanged.  The backward is
- * fa_bwd_dropout.  k, v have H_kv heads as in fa_fwd_gqa.  Arguments,
- * workspace and errors as for fa_fwd_splitkv_gqa, plus those of the dropout
- * parameters.
- */
-int fa_fwd_splitkv_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                           int causal, float scale, int dtype, int num_splits,
-                           float dropout_p, uint64_t seed, uint64_t offset,
-                           void* workspace, size_t workspace_bytes, void* stream);
-
-/*
- * fa_fwd_splitkv_masked -- the split-K/V forward (fa_fwd_splitkv_gqa) with a
- * key-padding mask given by its tile table, as in fa_fwd_masked: each split
- * takes its share of the batch element's list of non-empty key tiles, and a
- * row that sees no key in a split gets the -inf partial LSE the merge
- * weights by zero (a row with no visible key at all: O = 0, LSE = -inf).
- * dropout_p = 0: no dropout; 0 < dropout_p < 1: dropout as in
- * fa_fwd_masked_dropout.  Errors as for fa_fwd_splitkv_gqa and the dropout
- * calls, plus FA_ERR_NULL / FA_ERR_ALIGN for the table.
- */
-int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse,
-                          int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t D,
-                          int causal, float scale, int dtype, const void* tiles, int num_splits,
-                          float dropout_p, uint64_t seed, uint64_t offset,
-                          void* workspace, size_t workspace_bytes, void* stream);
-
-/*
- * fa_dropout_mask -- write the keep mask the dropout calls above use:
+ * fa_dropout_mask -- write the keep mask that dropout (fa_options) uses:
  * keep[b][h][i][j] = 1 (kept) or 0 (dropped), bytes, [B, H, N, N] on the
  * device (caller-owned, any alignment).  Meant for tests and inspection: it
  * is N*N bytes per head.  Errors: FA_ERR_NULL, FA_ERR_SHAPE (N > 2^24 or too
@@ -433,6 +242,127 @@ int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, 
  */
 int fa_dropout_mask(uint8_t* keep, int64_t B, int64_t H, int64_t N,
                     float dropout_p, uint64_t seed, uint64_t offset, void* stream);
+
+/*
+ * Options of one call: the features beyond plain multi-head attention, set
+ * in one struct instead of one entry point per combination.  Start from
+ * FA_OPTIONS_DEFAULT (plain attention: fa_fwd / fa_bwd) and set the fields a
+ * call uses; every combination is supported.  The backward of a forward
+ * takes the same options (num_splits aside: the backward of a split forward
+ * is the plain one).  A NULL options pointer means FA_OPTIONS_DEFAULT.
+ *
+ *   h_kv       : K/V heads (GQA; h_kv = 1 is MQA).  k, v (and dk, dv) are
+ *                [B, h_kv, N, D]; query head h of batch element b reads K/V
+ *                head h / (H / h_kv) of b in place, no copy ("CUDA
+ *                FlashAttention ...", §7: query heads map onto a shared K/V
+ *                head; the workgroups of one group are numbered onto the same
+ *                XCD when B*h_kv is a multiple of 8).  The gradient of a shared
+ *                K/V head is the sum over its H / h_kv query heads, added in
+ *                FP32 registers (and, when the dK/dV pass runs in parts, by a
+ *                reduce kernel in a fixed order): bitwise reproducible.
+ *                0 means H.  FA_ERR_SHAPE if h_kv < 0 or does not divide H.
+ *   mask_tiles : a key-padding mask as its tile table (fa_mask_tiles, same B
+ *                and N; contents trusted), or NULL for none.  Hidden keys get
+ *                dK = dV = 0 exactly; a row with no visible key gets O = 0,
+ *                LSE = -inf and dQ = 0.  FA_ERR_ALIGN if not 16-byte aligned.
+ *   dropout    : 1 = attention dropout with (dropout_p, dropout_seed,
+ *                dropout_offset) as defined above (p = 0 keeps every
+ *                probability but runs the dropout kernels); 0 = none.
+ *                FA_ERR_UNSUPPORTED for another value or p outside [0, 1).
+ *   num_splits : fa_fwd_ex only.  0 = one pass.  S in 1 .. 64: the keys are
+ *                split into S contiguous ranges of whole 64-key tiles ("CUDA
+ *                FlashAttention ...", §7: for long N and small B*H, split
+ *                along K; each part yields a local (m, l, o), merged with the
+ *                formula of §4).  Pass 1: one workgroup per (query tile,
+ *                split) writes each row's split LSE_s and its output O_s
+ *                normalised within the split (FP32, in the workspace; -inf
+ *                for a split with no visible key).  Pass 2: LSE = m + ln
+ *                sum_s exp(LSE_s - m), m = max_s LSE_s, and O = sum_s
+ *                exp(LSE_s - LSE) O_s, rounded to dtype (RNE).  With dropout
+ *                each split drops and scales its own probabilities and its
+ *                partial LSE is that of the undropped ones, so the merge
+ *                weights are unchanged; with a mask each split takes its
+ *                share of the batch element's list of non-empty key tiles.
+ *                FA_ERR_UNSUPPORTED outside 0 .. 64.
+ */
+typedef struct fa_options {
+  int64_t h_kv;
+  const void* mask_tiles;
+  int dropout;
+  float dropout_p;
+  uint64_t dropout_seed;
+  uint64_t dropout_offset;
+  int num_splits;
+} fa_options;
+
+#define FA_OPTIONS_DEFAULT {0, NULL, 0, 0.0f, 0, 0, 0}
+
+/*
+ * fa_fwd_splitkv_num_splits -- a split count for the split-K/V forward
+ * (fa_options.num_splits of fa_fwd_ex) on this
+ * shape ("CUDA FlashAttention ...", §7: split along K when N is long and
+ * B*H is small, so that there are enough workgroups).  The forward runs one
+ * workgroup per 128 queries, W = B*H*ceil(N/128) of them; the count doubles,
+ * from 1, while W*S < 512 (two workgroups per compute unit), each of the S
+ * ranges would keep at least 2048 keys after the doubling, and S < 16.
+ * Returns 1 when splitting would not pay (for example B=1 H=32 N=8192), and
+ * 0 for a shape fa_fwd would reject.  Host-only: no GPU work.
+ */
+int fa_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t D, int causal);
+
+/*
+ * fa_fwd_ex_workspace_bytes -- bytes of device workspace fa_fwd_ex needs with
+ * these options: for num_splits = S >= 1 an FP32 LSE and an FP32 D-vector per
+ * query row and split, S*B*H*N*(D+1)*4 (each part rounded up to 256); 0 when
+ * no workspace is needed (num_splits = 0) or for arguments fa_fwd_ex would
+ * reject.  Host-only.
+ */
+size_t fa_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
+                                 int causal, int dtype, const fa_options* opt);
+
+/*
+ * fa_fwd_ex -- fa_fwd with options (see fa_options).
+ *   k, v      : [B, h_kv, N, D]; q, o : [B, H, N, D]; lse : FP32 [B, H, N].
+ *   workspace : caller-owned device memory of at least
+ *               fa_fwd_ex_workspace_bytes(...) bytes, 16-byte aligned (may be
+ *               NULL when that is 0); contents on entry ignored, on return
+ *               unspecified.
+ * Other arguments, layouts and errors as for fa_fwd; additionally the option
+ * errors above and FA_ERR_WORKSPACE for a missing or short workspace.
+ * fa_fwd(...) is fa_fwd_ex(..., NULL, NULL, 0, stream).
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int64_t B, int64_t H, int64_t N, int64_t D,
+              int causal, float scale, int dtype, const fa_options* opt,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_ex_workspace_bytes -- bytes of device workspace fa_bwd_ex needs:
+ * Delta (4*B*H*N), plus, when the dK/dV pass splits the query positions of
+ * each K/V head (its G = H / h_kv query heads' query tiles) into P > 1 parts
+ * (few K/V heads: the pass would otherwise have too few workgroups to fill
+ * the GPU; P is at most the larger of G and the number of 8-tile groups of
+ * query tiles), FP32 partial dK and dV of 4*P*B*h_kv*N*D bytes each; and,
+ * when the dQ pass runs in parts, FP32 partial dQ likewise; sections rounded
+ * up to 256.  Equals fa_bwd_workspace_bytes for the default options; 0 for
+ * arguments fa_bwd_ex would reject.  Host-only.
+ */
+size_t fa_bwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
+                                 int causal, int dtype, const fa_options* opt);
+
+/*
+ * fa_bwd_ex -- fa_bwd for a forward computed by fa_fwd or fa_fwd_ex with the
+ * same options (num_splits is ignored).  dk, dv : [B, h_kv, N, D]; every
+ * other tensor as in fa_bwd.  Workspace: fa_bwd_ex_workspace_bytes(...).
+ * Errors as for fa_bwd plus the option errors above.
+ * fa_bwd(...) is fa_bwd_ex(..., NULL, workspace, workspace_bytes, stream).
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+              const float* lse, const void* dout,
+              void* dq, void* dk, void* dv,
+              int64_t B, int64_t H, int64_t N, int64_t D,
+              int causal, float scale, int dtype, const fa_options* opt,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /* fa_status_str -- a static, human-readable name for a status code. */
 const char* fa_status_str(int status);

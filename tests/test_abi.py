@@ -24,12 +24,30 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_gqa", "fa_bwd_gqa_workspace_bytes",
-                                    "fa_bwd_masked", "fa_bwd_masked_dropout", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd",
-                                    "fa_fwd_dropout", "fa_fwd_gqa", "fa_fwd_kernel_name", "fa_fwd_masked", "fa_fwd_masked_dropout", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_dropout", "fa_fwd_splitkv_gqa", "fa_fwd_splitkv_masked", "fa_fwd_splitkv_num_splits",
-                                    "fa_fwd_splitkv_workspace_bytes", "fa_mask_tiles", "fa_mask_tiles_bytes",
-                                    "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes", "fa_bwd_noalloc",
+                                    "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd", "fa_fwd_ex",
+                                    "fa_fwd_ex_workspace_bytes", "fa_fwd_kernel_name", "fa_fwd_splitkv_num_splits",
+                                    "fa_mask_tiles", "fa_mask_tiles_bytes", "fa_status_str"]
+
+
+def test_options_struct_layout_matches_the_header(tmp_path):
+    """The binding's FaOptions has the size and field offsets of struct
+    fa_options as a C compiler lays it out from include/fa.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    fields = [f[0] for f in fb.FaOptions._fields_]
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fa.h"\nint main(void) {\n'
+                   '  fa_options d = FA_OPTIONS_DEFAULT; (void)d;\n  printf("%zu", sizeof(fa_options));\n' +
+                   "".join('  printf(" %%zu", offsetof(fa_options, %s));\n' % f for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [ctypes.sizeof(fb.FaOptions)] + [getattr(fb.FaOptions, f).offset for f in fields]
 
 
 def test_library_exports_every_declared_symbol():
@@ -98,28 +116,88 @@ def test_workspace_bytes():
     assert fb.bwd_workspace_bytes(1, 1, 100, 96, 0, 0) == 0
 
 
-def split(**kw):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=256, D=128, causal=1, scale=0.1, dtype=1, s=4,
-             ws=P, wsb=1 << 30, stream=None)
+def fwd_ex(opt, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, N=256, D=64, causal=1, scale=0.125, dtype=0, ws=P, wsb=1 << 30)
     a.update(kw)
-    return fb.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"],
-                             a["causal"], a["scale"], a["dtype"], a["s"], a["ws"], a["wsb"], a["stream"])
+    return fb.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"], a["causal"],
+                        a["scale"], a["dtype"], opt, a["ws"], a["wsb"], None)
 
 
-@pytest.mark.parametrize("kw,code", [
-    (dict(q=None), 1), (dict(lse=None), 1), (dict(s=0), 3), (dict(s=65), 3), (dict(N=-200), 2),
-    (dict(ws=None), 5), (dict(wsb=1000), 5), (dict(ws=P + 8), 4), (dict(v=P + 2), 4), (dict(B=0), 2),
+def bwd_ex(opt, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=4, N=128, D=128, causal=0, scale=0.1,
+             dtype=1, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return fb.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["B"],
+                        a["H"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"], opt, a["ws"], a["wsb"], None)
+
+
+def bad_flag():
+    o = fb.options()
+    o.dropout = 2
+    return o
+
+
+ALL = dict(h_kv=2, tiles=P, dropout=(0.1, 1, 0))  # every option at once (a valid combination)
+
+
+@pytest.mark.parametrize("opt,kw,code", [
+    (None, dict(q=None), 1), (fb.options(), dict(lse=None), 1), (fb.options(**ALL, num_splits=3), dict(k=None), 1),
+    (fb.options(h_kv=3), {}, 2), (fb.options(h_kv=-1), {}, 2), (fb.options(h_kv=5), {}, 2),
+    (fb.options(**ALL), dict(N=-1), 2), (fb.options(**ALL, num_splits=2), dict(B=0), 2),
+    (fb.options(tiles=P + 4), {}, 4), (fb.options(**ALL), dict(o=P + 2), 4), (fb.options(h_kv=2), dict(v=P + 2), 4),
+    (bad_flag(), {}, 3), (fb.options(dropout=(1.0, 1, 0)), {}, 3), (fb.options(dropout=(-0.1, 1, 0)), {}, 3),
+    (fb.options(dropout=(float("nan"), 1, 0)), {}, 3), (fb.options(**ALL), dict(D=80), 3),
+    (fb.options(num_splits=65), {}, 3), (fb.options(num_splits=-1), {}, 3),
+    (fb.options(num_splits=4), dict(ws=None), 5), (fb.options(**ALL, num_splits=4), dict(wsb=1000), 5),
+    (fb.options(num_splits=4), dict(ws=P + 8), 4),
 ])
-def test_splitkv_rejects(kw, code):
-    assert split(**kw) == code
+def test_fwd_ex_rejects(opt, kw, code):
+    assert fwd_ex(opt, **kw) == code
 
 
-def test_splitkv_workspace_bytes():
+@pytest.mark.parametrize("opt,kw,code", [
+    (None, dict(dq=None), 1), (fb.options(**ALL), dict(dk=None), 1),
+    (fb.options(h_kv=3), {}, 2), (fb.options(**ALL), dict(H=0), 2),
+    (fb.options(tiles=P + 4), {}, 4), (fb.options(**ALL), dict(ws=P + 4), 4),
+    (fb.options(dropout=(1.5, 1, 0)), {}, 3), (bad_flag(), {}, 3), (fb.options(**ALL), dict(dtype=3), 3),
+    (fb.options(**ALL), dict(ws=None), 5), (fb.options(h_kv=1), dict(wsb=4 * 4 * 128 - 1), 5),
+])
+def test_bwd_ex_rejects(opt, kw, code):
+    assert bwd_ex(opt, **kw) == code
+
+
+def test_fwd_ex_workspace_bytes():
     rows = 2 * 3 * 128 * 4
-    assert fb.fwd_splitkv_workspace_bytes(2, 3, 128, 64, 1, 0, 4) == rows * 4 + rows * 64 * 4
-    assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 1) == 256 + 64 * 128 * 4
-    assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 0) == 0
-    assert fb.fwd_splitkv_workspace_bytes(1, 1, 64, 128, 0, 0, 65) == 0
+    assert fb.fwd_ex_workspace_bytes(2, 3, 128, 64, 1, 0, fb.options(num_splits=4)) == rows * 4 + rows * 64 * 4
+    assert fb.fwd_ex_workspace_bytes(1, 1, 64, 128, 0, 0, fb.options(num_splits=1)) == 256 + 64 * 128 * 4
+    # with grouped heads and the other options the states are still per query head
+    rows = 2 * 4 * 300 * 3  # 28800 bytes of LSE, rounded up to 28928
+    assert fb.fwd_ex_workspace_bytes(2, 4, 300, 64, 1, 0, fb.options(h_kv=2, tiles=P, dropout=(0.1, 1, 0),
+                                                                     num_splits=3)) == 28928 + rows * 64 * 4
+    # one pass needs none; rejected options give 0
+    assert fb.fwd_ex_workspace_bytes(1, 1, 64, 128, 0, 0, None) == 0
+    assert fb.fwd_ex_workspace_bytes(1, 1, 64, 128, 0, 0, fb.options(num_splits=0)) == 0
+    assert fb.fwd_ex_workspace_bytes(1, 1, 64, 128, 0, 0, fb.options(num_splits=65)) == 0
+    assert fb.fwd_ex_workspace_bytes(1, 4, 64, 128, 0, 0, fb.options(h_kv=3, num_splits=2)) == 0
+
+
+def test_bwd_ex_workspace_bytes():
+    kv = lambda h: fb.options(h_kv=h)
+    # H_kv = H (or no options): Delta only, as fa_bwd_workspace_bytes
+    assert fb.bwd_ex_workspace_bytes(2, 4, 100, 64, 1, 0, kv(4)) == fb.bwd_workspace_bytes(2, 4, 100, 64, 1, 0)
+    assert fb.bwd_ex_workspace_bytes(2, 4, 100, 64, 1, 0, None) == fb.bwd_workspace_bytes(2, 4, 100, 64, 1, 0)
+    # enough workgroups (B*H_kv*ceil(N/128) >= 1024): one part, Delta only
+    assert fb.bwd_ex_workspace_bytes(1, 64, 16384, 128, 1, 0, kv(8)) == 64 * 16384 * 4
+    # MQA, B1 H32 N8192: 64 workgroups -> 16 parts of FP32 dK and dV partials
+    delta = 32 * 8192 * 4
+    part = 16 * 8192 * 128 * 4
+    assert fb.bwd_ex_workspace_bytes(1, 32, 8192, 128, 1, 0, kv(1)) == delta + 2 * part
+    # parts never exceed the group size
+    assert fb.bwd_ex_workspace_bytes(1, 2, 64, 64, 0, 1, kv(1)) == 2 * 64 * 4 + 2 * 2 * 64 * 64 * 4
+    assert fb.bwd_ex_workspace_bytes(1, 4, 64, 64, 0, 0, kv(3)) == 0
+    # the mask and dropout options need no more; num_splits is ignored by the backward
+    assert fb.bwd_ex_workspace_bytes(1, 32, 8192, 128, 1, 0, fb.options(h_kv=1, tiles=P, dropout=(0.2, 3, 4),
+                                                                        num_splits=99)) == delta + 2 * part
 
 
 @pytest.mark.parametrize("shape,splits", [
@@ -152,142 +230,12 @@ def test_mask_tiles_rejects(kw, code):
     assert fb.fa_mask_tiles(a["mask"], a["B"], a["N"], a["tiles"], a["nb"], None) == code
 
 
-@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 4), 4), (dict(q=None), 1),
-                                     (dict(D=80), 3), (dict(N=-1), 2), (dict(o=P + 2), 4), (dict(Hkv=3), 2),
-                                     (dict(Hkv=0), 2)])
-def test_fwd_masked_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Hkv=2, N=128, D=64, causal=1, scale=0.125, dtype=0, tiles=P)
-    a.update(kw)
-    assert fb.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["D"],
-                            a["causal"], a["scale"], a["dtype"], a["tiles"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 4), 4), (dict(dk=None), 1),
-                                     (dict(ws=None), 5), (dict(dtype=3), 3)])
-def test_bwd_masked_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, Hkv=1, N=128, D=64, causal=1,
-             scale=0.125, dtype=0, tiles=P, ws=P, wsb=1 << 20)
-    a.update(kw)
-    assert fb.fa_bwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
-                            a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"],
-                            a["tiles"], a["ws"], a["wsb"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(Hkv=0), 2), (dict(Hkv=3), 2), (dict(Hkv=5), 2), (dict(H=0), 2),
-                                     (dict(k=None), 1), (dict(v=P + 2), 4), (dict(D=32), 3)])
-def test_fwd_gqa_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=128, D=64, causal=1, scale=0.125, dtype=0)
-    a.update(kw)
-    assert fb.fa_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["D"],
-                         a["causal"], a["scale"], a["dtype"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(Hkv=3), 2), (dict(dv=None), 1), (dict(ws=None), 5),
-                                     (dict(wsb=4 * 4 * 128 - 1), 5)])
-def test_bwd_gqa_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=4, Hkv=1, N=128, D=64, causal=0,
-             scale=0.125, dtype=1, ws=P, wsb=1 << 20)
-    a.update(kw)
-    assert fb.fa_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
-                         a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"],
-                         a["ws"], a["wsb"], None) == code
-
-
-def test_bwd_gqa_workspace_bytes():
-    # H_kv = H: Delta only, as fa_bwd_workspace_bytes
-    assert fb.bwd_gqa_workspace_bytes(2, 4, 4, 100, 64, 1, 0) == fb.bwd_workspace_bytes(2, 4, 100, 64, 1, 0)
-    # enough workgroups (B*H_kv*ceil(N/128) >= 1024): one part, Delta only
-    assert fb.bwd_gqa_workspace_bytes(1, 64, 8, 16384, 128, 1, 0) == 64 * 16384 * 4
-    # MQA, B1 H32 N8192: 64 workgroups -> 16 parts of FP32 dK and dV partials
-    delta = 32 * 8192 * 4
-    part = 16 * 8192 * 128 * 4
-    assert fb.bwd_gqa_workspace_bytes(1, 32, 1, 8192, 128, 1, 0) == delta + 2 * part
-    # parts never exceed the group size
-    assert fb.bwd_gqa_workspace_bytes(1, 2, 1, 64, 64, 0, 1) == 2 * 64 * 4 + 2 * 2 * 64 * 64 * 4
-    assert fb.bwd_gqa_workspace_bytes(1, 4, 3, 64, 64, 0, 0) == 0
-
-
-@pytest.mark.parametrize("kw,code", [(dict(p=1.0), 3), (dict(p=-0.1), 3), (dict(p=float("nan")), 3),
-                                     (dict(q=None), 1), (dict(Hkv=3), 2), (dict(lse=P + 4), 4)])
-def test_fwd_dropout_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=128, D=64, causal=1, scale=0.125, dtype=0, p=0.1,
-             seed=1, offset=0)
-    a.update(kw)
-    assert fb.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["D"],
-                             a["causal"], a["scale"], a["dtype"], a["p"], a["seed"], a["offset"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(p=1.5), 3), (dict(ws=None), 5), (dict(dq=None), 1)])
-def test_bwd_dropout_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, Hkv=2, N=128, D=128, causal=0,
-             scale=0.1, dtype=1, p=0.2, seed=(1 << 64) - 1, offset=3, ws=P, wsb=1 << 20)
-    a.update(kw)
-    assert fb.fa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
-                             a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"], a["p"],
-                             a["seed"], a["offset"], a["ws"], a["wsb"], None) == code
-
-
 @pytest.mark.parametrize("kw,code", [(dict(keep=None), 1), (dict(N=0), 2), (dict(N=(1 << 24) + 1), 2),
                                      (dict(p=1.0), 3)])
 def test_dropout_mask_rejects(kw, code):
     a = dict(keep=P, B=1, H=1, N=64, p=0.5, seed=1, offset=0)
     a.update(kw)
     assert fb.fa_dropout_mask(a["keep"], a["B"], a["H"], a["N"], a["p"], a["seed"], a["offset"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 8), 4), (dict(p=1.0), 3),
-                                     (dict(q=None), 1), (dict(Hkv=3), 2)])
-def test_fwd_masked_dropout_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=128, D=64, causal=1, scale=0.125, dtype=0, tiles=P,
-             p=0.1, seed=1, offset=0)
-    a.update(kw)
-    assert fb.fa_fwd_masked_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
-                                    a["D"], a["causal"], a["scale"], a["dtype"], a["tiles"], a["p"], a["seed"],
-                                    a["offset"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(p=-1.0), 3), (dict(ws=None), 5),
-                                     (dict(dk=None), 1)])
-def test_bwd_masked_dropout_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, Hkv=2, N=128, D=128, causal=0,
-             scale=0.1, dtype=1, tiles=P, p=0.2, seed=5, offset=3, ws=P, wsb=1 << 20)
-    a.update(kw)
-    assert fb.fa_bwd_masked_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
-                                    a["B"], a["H"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"], a["dtype"],
-                                    a["tiles"], a["p"], a["seed"], a["offset"], a["ws"], a["wsb"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(s=0), 3), (dict(p=1.0), 3), (dict(p=-0.5), 3), (dict(p=float("nan")), 3),
-                                     (dict(ws=None), 5), (dict(wsb=1000), 5), (dict(q=None), 1), (dict(o=P + 8), 4),
-                                     (dict(Hkv=3), 2)])
-def test_splitkv_dropout_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=256, D=128, causal=1, scale=0.1, dtype=1, s=4, p=0.1,
-             seed=1, offset=0, ws=P, wsb=1 << 30)
-    a.update(kw)
-    assert fb.fa_fwd_splitkv_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
-                                     a["D"], a["causal"], a["scale"], a["dtype"], a["s"], a["p"], a["seed"],
-                                     a["offset"], a["ws"], a["wsb"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(Hkv=3), 2), (dict(Hkv=0), 2), (dict(s=65), 3), (dict(ws=None), 5),
-                                     (dict(k=None), 1)])
-def test_splitkv_gqa_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, N=256, D=64, causal=0, scale=0.1, dtype=0, s=2,
-             ws=P, wsb=1 << 30)
-    a.update(kw)
-    assert fb.fa_fwd_splitkv_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["D"],
-                                 a["causal"], a["scale"], a["dtype"], a["s"], a["ws"], a["wsb"], None) == code
-
-
-@pytest.mark.parametrize("kw,code", [(dict(tiles=None), 1), (dict(tiles=P + 4), 4), (dict(p=1.0), 3), (dict(p=-0.1), 3),
-                                     (dict(s=0), 3), (dict(ws=None), 5), (dict(Hkv=3), 2)])
-def test_splitkv_masked_rejects(kw, code):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, Hkv=2, N=300, D=64, causal=1, scale=0.1, dtype=0, tiles=P, s=3,
-             p=0.0, seed=0, offset=0, ws=P, wsb=1 << 30)
-    a.update(kw)
-    assert fb.fa_fwd_splitkv_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
-                                    a["D"], a["causal"], a["scale"], a["dtype"], a["tiles"], a["s"], a["p"],
-                                    a["seed"], a["offset"], a["ws"], a["wsb"], None) == code
 
 
 CLIENT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_client")

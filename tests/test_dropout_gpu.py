@@ -1,6 +1,6 @@
 """Attention dropout on the GPU: the keep mask regenerated from (seed,
 offset) by fa_dropout_mask (bit-exact against the oracle's Philox4x64-10
-mapping), and fa_fwd_dropout / fa_bwd_dropout (through the C ABI) against
+mapping), and fa_fwd_ex / fa_bwd_ex with fa_options.dropout (through the C ABI) against
 the float64 oracle with the same (p, seed, offset).  "Why FlashAttention does
 not need to store the attention matrix" §05: only the seed and offset are
 kept; the backward pass regenerates the mask."""
@@ -153,8 +153,8 @@ def test_dropout_bwd_one_head_in_parts():
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("kind", ["lengths", "blocks", "random"])
 def test_dropout_with_key_mask(kind, D, causal, dtype):
-    # dropout and a key-padding mask together (fa_fwd_masked_dropout,
-    # fa_bwd_masked_dropout) against the oracle with both applied; the random
+    # dropout and a key-padding mask together (both options of fa_fwd_ex /
+    # fa_bwd_ex) against the oracle with both applied; the random
     # mask hides keys 0..2 so that causal rows 0..2 see no key at all
     B, H, N = 2, 2, 333
     say("dropout + %s mask D=%d causal=%d %s" % (kind, D, causal, dtype))

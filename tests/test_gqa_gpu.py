@@ -1,5 +1,5 @@
-"""Grouped K/V heads (GQA; MQA when H_kv = 1) on the GPU: fa_fwd_gqa and
-fa_bwd_gqa (through the C ABI, via fa.fwd / fa.bwd with k, v of H_kv heads)
+"""Grouped K/V heads (GQA; MQA when H_kv = 1) on the GPU: fa_fwd_ex and
+fa_bwd_ex with fa_options.h_kv (through the C ABI, via fa.fwd / fa.bwd with k, v of H_kv heads)
 against the float64 oracle, whose grouped-head reading is pinned against
 repeated K/V heads.  "CUDA FlashAttention ..." §7: query heads share a K/V
 head in place, without copying K or V."""
@@ -119,7 +119,7 @@ def test_bwd_gqa_uneven_head_parts():
     # B*H_kv*ceil(N/128) = 256 workgroups -> the dK/dV pass splits each group
     # of G = 6 query heads into 4 parts of 1, 2, 1, 2 heads
     B, H, Hkv, N, D = 8, 12, 2, 2048, 64
-    assert fa.bwd_gqa_workspace_bytes(B, H, Hkv, N, D, 1, 0) == B * H * N * 4 + 2 * 4 * B * Hkv * N * D * 4
+    assert fa.bwd_ex_workspace_bytes(B, H, N, D, 1, 0, fa.options(h_kv=Hkv)) == B * H * N * 4 + 2 * 4 * B * Hkv * N * D * 4
     inp = gqa_inputs(B, H, Hkv, N, D, "fp16", 6500)
     q, k, v, do = (to_dev(inp[n], "fp16") for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, causal=True)

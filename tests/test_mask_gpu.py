@@ -1,6 +1,6 @@
 """Key-padding masks on the GPU: the tile table built by fa_mask_tiles
-(bit-exact against the oracle's block-level words), fa_fwd_masked and
-fa_bwd_masked (through the C ABI) against the float64 oracle with the same
+(bit-exact against the oracle's block-level words), fa_fwd_ex and
+fa_bwd_ex with fa_options.mask_tiles (through the C ABI) against the float64 oracle with the same
 mask.  Masks follow "FlashAttention dataflow and engineering validation on
 MI50": padded variable-length batches (§4.3) and random mask patterns
 (§5.1), plus tile-structured masks that give the block-level flags every

@@ -1,5 +1,5 @@
 """Sequence lengths that are not a multiple of the 64-row tile, on the GPU:
-fa_fwd, fa_fwd_splitkv and fa_bwd (through the C ABI) against the float64
+fa_fwd, the split-K/V fa_fwd_ex and fa_bwd (through the C ABI) against the float64
 oracle, and guard regions after every output that must stay untouched.
 
 "FlashAttention dataflow and engineering validation on MI50" (§6.1) names the
@@ -139,7 +139,7 @@ def test_rows_past_the_end_are_never_read(N, D, causal, dtype):
     """The partial last K/V tile of the last head is followed by memory that
     is not the caller's: only its valid rows may reach the result.  Every
     input sits at the start of a buffer that continues with NaN, and
-    fa_fwd, fa_fwd_splitkv and fa_bwd must still match the oracle."""
+    fa_fwd, the split fa_fwd_ex and fa_bwd must still match the oracle."""
     say("rows past the end N=%d D=%d causal=%d %s" % (N, D, causal, dtype))
     inp = make_inputs(1, 2, N, D, dtype, seed=4500 + N + D, with_dout=True)
     scale = 1.0 / np.sqrt(D)
@@ -151,7 +151,7 @@ def test_rows_past_the_end_are_never_read(N, D, causal, dtype):
     assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, dtype, "fa_fwd N=%d D=%d" % (N, D))
     o2, lse2 = fa.fwd_splitkv(q, k, v, 3, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    assert_fwd_close(to_host(o2), to_host(lse2), o_ref, lse_ref, dtype, "fa_fwd_splitkv N=%d D=%d" % (N, D))
+    assert_fwd_close(to_host(o2), to_host(lse2), o_ref, lse_ref, dtype, "split fa_fwd_ex N=%d D=%d" % (N, D))
     o_t = nan_tailed(o.shape, o.dtype).copy_(o)
     lse_t = nan_tailed(lse.shape + (1,), torch.float32).view(lse.shape).copy_(lse)
     grads = fa.bwd(q, k, v, o_t, lse_t, do, causal=causal, scale=scale)

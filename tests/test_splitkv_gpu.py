@@ -1,4 +1,4 @@
-"""Split-K/V forward parity on the GPU: fa_fwd_splitkv (through the C ABI)
+"""Split-K/V forward parity on the GPU: fa_fwd_ex with fa_options.num_splits (through the C ABI)
 against the float64 oracle, for split counts that leave some ranges empty."""
 
 import numpy as np
@@ -98,8 +98,8 @@ def test_splitkv_with_dropout(splits, causal, D):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("with_dropout", [False, True])
 def test_splitkv_grouped_heads(with_dropout, causal, Hkv):
-    # grouped K/V heads through the split forward (fa_fwd_splitkv_gqa, and
-    # fa_fwd_splitkv_dropout with H_kv < H) against the oracle
+    # grouped K/V heads through the split forward (num_splits with h_kv, and
+    # with dropout too) against the oracle
     B, H, N, D = 2, 4, 900, 128
     rng = np.random.default_rng(3300 + Hkv + causal + with_dropout)
     q = round_to(rng.standard_normal((B, H, N, D), dtype=np.float32), "fp16")
