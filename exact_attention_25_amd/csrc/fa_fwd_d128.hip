@@ -22,9 +22,10 @@
 //    Inline assembly is opaque to the compiler's hazard checks, so the wait
 //    states gfx950 requires are placed by hand: 12 between an MFMA that
 //    writes a register and a vector instruction that reads it (16 are used:
-//    after each batch of score MFMAs, and before O is read), and 2 between a
-//    vector write and an MFMA reading that register as an operand (before the
-//    first P V MFMA of every freshly packed probability operand).
+//    after each batch of score MFMAs, and before O is read).  A vector write
+//    needs 2 before an MFMA reads that register; every probability operand
+//    is packed at least eight slots before its first P V MFMA, so none are
+//    placed there (the test suite scans the generated code for both).
 //  * With one wave per SIMD nothing hides a stall, so a step of the tile loop
 //    is written as 64 MFMA slots with the other work placed beside them (see
 //    the step below): no LDS read, barrier or copy waits on data issued just
@@ -213,6 +214,18 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
         }
     }
   };
+  // Row maxima of both query blocks across the two lane halves: one swap
+  // exchanges the halves of the two values (lanes 0-31 then see block 0 in
+  // both registers, lanes 32-63 block 1), a second spreads each block's
+  // result to every lane.  med3(x, y, +inf) is max(x, y) without the
+  // canonicalising moves fmaxf adds.
+  auto xhalf_max2 = [&](float a0, float a1, float& m0, float& m1) __attribute__((always_inline)) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+    const float t = __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), INFINITY);
+    auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    m0 = __uint_as_float(u[0]);
+    m1 = __uint_as_float(u[1]);
+  };
   auto needs_mask = [&](int k0) { return (CAUSAL && k0 + kBN - 1 > q0w) || k0 + kBN > N; };
   float mx[2];
   auto tile_max = [&](const f32x16 (&s)[2][2]) __attribute__((always_inline)) {
@@ -316,6 +329,9 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
     for (int i = 0; i < 2 * NS; ++i) {
       const int qb = i & 1, f = i >> 1;
       if (qb == 0 && f + PK < NS) kq[(f + PK) % (PK + 1)] = kread(kbA, f + PK);
+      // One LDS wait per two fragments: before fragment f's first MFMA (f
+      // even) wait for fragment f+1 as well.
+      if (qb == 0 && (f & 1) == 0) asm volatile("" ::"v"(kq[(f + 1) % (PK + 1)]));
       if (f < 2)
         mfma_s_first<T>(s_nxt[qb][f & 1], kq[f % (PK + 1)], qa[qb][f >> 1]);
       else
@@ -345,7 +361,8 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
     scores_ready(s_nxt);
 
     // ---- phase B ----
-    float lsum[2] = {0.f, 0.f}, lsum2[2] = {0.f, 0.f}, mn[2] = {-INFINITY, -INFINITY};
+    float lsum[2], lsum2[2], mn[2] = {-INFINITY, -INFINITY};
+    if constexpr (T::id != Fp16::id) lsum[0] = lsum[1] = 0.f;
 #pragma unroll
     for (int i = 0; i < 2 * NV; ++i) {
       const int qb = i & 1, v = i >> 1, t = v / (kD / 32), db = v % (kD / 32);
@@ -354,10 +371,8 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
         barrier_only();
       }
       if (qb == 0 && v + PV < NV) vq[(v + PV) % (PV + 1)] = vread(vbB, v + PV);
-      if (db == 0)
-        mfma_o<T, true>(oacc[qb][db], vq[v % (PV + 1)], pf[qb][t]);
-      else
-        mfma_o<T, false>(oacc[qb][db], vq[v % (PV + 1)], pf[qb][t]);
+      if (qb == 0 && (v & 1) == 0) asm volatile("" ::"v"(vq[(v + 1) % (PV + 1)]));
+      mfma_o<T, false>(oacc[qb][db], vq[v % (PV + 1)], pf[qb][t]);
       if (i < 24) {  // operand 1 + i/8, dword (i/2) % 4 of block qb
         const int tp = 1 + (i >> 3), w = (i >> 1) & 3;
         const int lo = (tp & 1) * 8 + 2 * w;
@@ -370,10 +385,16 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
           // v_fma_mix of a slot do not wait for each other.  (Adding dword
           // pairs as fp16 first saves instructions but its extra rounding
           // was measured to cost accuracy.)
-          asm("v_fma_mix_f32 %0, %2, 1.0, %0 op_sel_hi:[1,0,0]\n\t"
-              "v_fma_mix_f32 %1, %2, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-              : "+v"(lsum[qb]), "+v"(lsum2[qb])
-              : "v"(pf[qb][d >> 2][d & 3]));
+          if (d == 0)  // the first dword starts both sums
+            asm("v_fma_mix_f32 %0, %2, 1.0, 0 op_sel_hi:[1,0,0]\n\t"
+                "v_fma_mix_f32 %1, %2, 1.0, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                : "=&v"(lsum[qb]), "=&v"(lsum2[qb])
+                : "v"(pf[qb][0][0]));
+          else
+            asm("v_fma_mix_f32 %0, %2, 1.0, %0 op_sel_hi:[1,0,0]\n\t"
+                "v_fma_mix_f32 %1, %2, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                : "+v"(lsum[qb]), "+v"(lsum2[qb])
+                : "v"(pf[qb][d >> 2][d & 3]));
           asm volatile("" : "+v"(lsum2[qb]));
         } else {
           const int lo = ((d >> 2) & 1) * 8 + 2 * (d & 3);
@@ -395,10 +416,8 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      l_run[qb] += lsum[qb] + lsum2[qb];
-      mx[qb] = xhalf_max(mn[qb]);
-    }
+    for (int qb = 0; qb < 2; ++qb) l_run[qb] += T::id == Fp16::id ? lsum[qb] + lsum2[qb] : lsum[qb];
+    xhalf_max2(mn[0], mn[1], mx[0], mx[1]);
     // The row max of tile j+1 was taken beside the MFMAs (with no branch
     // between the phases, so that nothing is moved out of its slot); a tile
     // that needs a mask is masked now and its max taken again.
