@@ -224,6 +224,11 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
     m1 = __uint_as_float(u[1]);
   };
   auto needs_mask = [&](int k0) { return (CAUSAL && k0 + kBN - 1 > q0w) || k0 + kBN > N; };
+  // mx: a tile's row max over this lane's half of the keys (the two lanes
+  // of a query each hold one half).  The rescale decision needs no more:
+  // max(h0, h1) * c2 > t exactly when h0 * c2 > t or h1 * c2 > t (c2 > 0,
+  // rounding is monotone), and the vote covers both lanes.  Only a rescale
+  // takes the full max, so the common path has no lane-half exchange.
   float mx[2];
   auto tile_max = [&](const f32x16 (&s)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
       for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, s[qb][1][r]);
-      mx[qb] = xhalf_max(m);
+      mx[qb] = m;
     }
   };
 
@@ -253,11 +258,12 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
     d_rescale = wave_any(need);
   };
   auto rescale = [&]() __attribute__((always_inline)) {
-    float r_new[2];
+    float r_new[2], m_full[2];
+    xhalf_max2(mx[0], mx[1], m_full[0], m_full[1]);
     bool big = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      r_new[qb] = fmaxf(r_raw[qb], mx[qb]);
+      r_new[qb] = fmaxf(r_raw[qb], m_full[qb]);
       const float nm = r_new[qb] * c2;
       big = big || (fabsf(nm) >= kFastLimit && nm != -INFINITY);
     }
@@ -417,7 +423,8 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) l_run[qb] += T::id == Fp16::id ? lsum[qb] + lsum2[qb] : lsum[qb];
-    xhalf_max2(mn[0], mn[1], mx[0], mx[1]);
+    mx[0] = mn[0];
+    mx[1] = mn[1];
     // The row max of tile j+1 was taken beside the MFMAs (with no branch
     // between the phases, so that nothing is moved out of its slot); a tile
     // that needs a mask is masked now and its max taken again.
