@@ -211,6 +211,10 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
 
   // Raw max over the tile of the pending scores, per query row; carried from
   // the step that computed those scores to the step that exponentiates them.
+  // mx: a tile's row max over this lane's half of the keys (the two lanes
+  // of a query each hold one half).  The rescale vote needs no more: with
+  // scale > 0, max(h0, h1) * c2 > t exactly when h0 * c2 > t or h1 * c2 > t,
+  // and the vote covers both lanes; only a rescale takes the full max.
   float mx[QB];
 
   // Mask of a tile's raw scores before its max: diagonal, partial last or
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, s[qb][1][r]);
-      mx[qb] = xhalf_max(m);
+      mx[qb] = m;
     }
   };
 
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
       bool big = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        r_new[qb] = fmaxf(r_raw[qb], mx[qb]);
+        r_new[qb] = fmaxf(r_raw[qb], xhalf_max(mx[qb]));
         const float nm = r_new[qb] * c2;
         big = big || (fabsf(nm) >= kFastLimit && nm != -INFINITY);
       }
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(kFwdThreads, QB == 1 ? 2 : 1) void fwd_kernel(FwdAr
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         l_run[qb] += lsum[qb];
-        mx[qb] = xhalf_max(mn[qb]);
+        mx[qb] = mn[qb];
       }
       decide();
     };
