@@ -240,7 +240,9 @@ __global__ __launch_bounds__(kShortThreads, QB == 1 ? 2 : 1) void fwd_short_kern
         m4[2] = fmaxf(m4[2], s[qb][1][r]);
         m4[3] = fmaxf(m4[3], s[qb][1][r + 1]);
       }
-      mx[qb] = xhalf_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      // This lane's half of the keys: enough for the vote (scale > 0, so the
+      // full max crosses the threshold exactly when one half does).
+      mx[qb] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
       need = need || (mx[qb] * c2 > mlazy[qb]);
     }
     if (wave_any(need)) {
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(kShortThreads, QB == 1 ? 2 : 1) void fwd_short_kern
       bool big = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        r_new[qb] = fmaxf(r_raw[qb], mx[qb]);
+        r_new[qb] = fmaxf(r_raw[qb], xhalf_max(mx[qb]));
         const float nm = r_new[qb] * c2;
         big = big || (fabsf(nm) >= kShortFastLimit && nm != -INFINITY);
       }
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(kShortThreads, 1) void fwd_short_pipe_kernel(FwdArg
   // tile of this block has been accumulated yet, so O and l are still zero.
   auto decide = [&](int qb, bool first) __attribute__((always_inline)) {
     if (wave_any(mx[qb] * c2 > mlazy[qb])) {
-      const float r_new = fmaxf(r_raw[qb], mx[qb]);
+      const float r_new = fmaxf(r_raw[qb], xhalf_max(mx[qb]));
       const float nm = r_new * c2;
       const bool raw_new = wave_any(fabsf(nm) >= kShortFastLimit && nm != -INFINITY);
       if (!first) {
@@ -634,7 +636,9 @@ __global__ __launch_bounds__(kShortThreads, 1) void fwd_short_pipe_kernel(FwdArg
     for (int c = 0; c < 4; ++c) ls[c] = 0.f;
   };
   auto fold_max = [&]() __attribute__((always_inline)) {
-    return xhalf_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+    // This lane's half of the keys: enough for the rescale vote, which
+    // exchanges lane halves only when it raises the reference.
+    return fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
   };
   auto fold_sum = [&]() __attribute__((always_inline)) { return (ls[0] + ls[1]) + (ls[2] + ls[3]); };
 
