@@ -91,7 +91,8 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
 
   // Q^T operand fragments in AGPRs: lane (ql, g) of block qb holds
   // Q[q0w + 32qb + ql][16c + 8g .. +8]; rows past N re-read row N-1.
-  // All sixteen loads are issued before the first is moved to an AGPR.
+  // All sixteen loads are issued here; they are bound to the AGPRs only
+  // after the first tile copies have been issued (see the prologue).
   u32x4 qa[2][kD / 16], qv[2][kD / 16];
   if (active) {
 #pragma unroll
@@ -106,11 +107,6 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
 #pragma unroll
       for (int c = 0; c < kD / 16; ++c) qv[qb][c] = u32x4{0, 0, 0, 0};
   }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int c = 0; c < kD / 16; ++c) asm volatile("s_nop 1" : "=a"(qa[qb][c]) : "0"(qv[qb][c]));
 
   f32x16 oacc[2][kD / 32];
   float r_raw[2], l_run[2];
@@ -450,6 +446,13 @@ __global__ __launch_bounds__(kNT, 1) void fwd_d128_kernel(FwdArgs a) {
     copy_v(1, 1, p);
     copy_k(2, 2, p);
   }
+  // Q reaches its AGPRs only now, so that its loads and the first tile
+  // copies are in flight together.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int c = 0; c < kD / 16; ++c) asm volatile("s_nop 1" : "=a"(qa[qb][c]) : "0"(qv[qb][c]));
   wait_vmem();
   __syncthreads();
   if (active) {
