@@ -51,6 +51,22 @@ def test_bwd_workload_all_heads():
         assert worst[0] <= GRAD_REL_TOL
 
 
+def test_bwd_headline_shape_all_heads():
+    """The backward at the shapes whose throughput the bench reports beside
+    the forward (causal fp16 B1 H32 N8192 D128, with a seeded dO): dQ, dK,
+    dV against the oracle over every head."""
+    w = workloads.CAUSAL_D128[8192]
+    say("bwd headline shape %s, all heads" % w.name)
+    inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, with_dout=True)
+    got = [to_host(t) for t in run_fwd_bwd(inp, w.dtype, w.causal, w.scale)]
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], w.causal, w.scale)
+    assert_grads_close(got, ref, "%s bwd, all %d heads" % (w.name, w.B * w.H))
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        worst = max((rel_fro(g[b, h], r[b, h]), b, h) for b in range(w.B) for h in range(w.H))
+        say("  %s worst head (%d,%d): relative Frobenius error %.3e" % (name, worst[1], worst[2], worst[0]))
+        assert worst[0] <= GRAD_REL_TOL
+
+
 def test_bwd_scale_and_bf16_long_rows():
     inp = make_inputs(1, 2, 1024, 128, "bf16", seed=77, spiky_keys=True, with_dout=True)
     got = [to_host(t) for t in run_fwd_bwd(inp, "bf16", True, 0.2)]
