@@ -67,6 +67,23 @@ def test_bwd_headline_shape_all_heads():
         assert worst[0] <= GRAD_REL_TOL
 
 
+def test_bwd_long_bf16_sampled_heads():
+    """The backward of the long bf16 workload (causal B1 H16 N32768 D128,
+    every 64th key scaled by 8) on the GPU over all heads; dQ, dK, dV of its
+    first and last heads -- whole heads, since dK and dV sum over every
+    query -- against the oracle."""
+    w = workloads.LONG_BF16
+    say("bwd %s, heads 0 and %d against the oracle" % (w.name, w.H - 1))
+    inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys, with_dout=True)
+    got = [to_host(t) for t in run_fwd_bwd(inp, w.dtype, w.causal, w.scale)]
+    hs = [0, w.H - 1]
+    for name, g in zip(("dQ", "dK", "dV"), got):
+        assert np.all(np.isfinite(g)), name
+    sub = {n: np.ascontiguousarray(inp[n][:, hs]) for n in ("q", "k", "v", "do")}
+    ref = attention_backward(sub["q"], sub["k"], sub["v"], sub["do"], w.causal, w.scale)
+    assert_grads_close([g[:, hs] for g in got], ref, "%s, heads %s" % (w.name, hs))
+
+
 def test_bwd_scale_and_bf16_long_rows():
     inp = make_inputs(1, 2, 1024, 128, "bf16", seed=77, spiky_keys=True, with_dout=True)
     got = [to_host(t) for t in run_fwd_bwd(inp, "bf16", True, 0.2)]
