@@ -62,7 +62,7 @@ def _sample_rows(n, count, rng):
 
 
 WORKLOADS = [workloads.SMALL, workloads.NONCAUSAL_D64, *workloads.CAUSAL_D128.values(),
-             workloads.FWDBWD_D64, workloads.LONG_BF16]
+             workloads.FWDBWD_D64, workloads.LONG_BF16, workloads.FEW_HEADS_LONG]
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
@@ -87,9 +87,9 @@ def test_fwd_causal_long_keys_one_tile_per_cu(dtype):
 def test_fwd_workload(w):
     """The whole output of every head against the oracle (the golden-reference
     comparison of "FlashAttention dataflow and engineering validation on
-    MI50", §5.1).  The long bf16 workload (N = 32768) compares 512 sampled
-    query rows -- the first and last 64, every 64th, the rest random -- of
-    every one of its heads."""
+    MI50", §5.1).  The workloads with N above 8192 (the long bf16 one and the
+    one-head N = 16384 one) compare 512 sampled query rows -- the first and
+    last 64, every 64th, the rest random -- of every one of their heads."""
     say("fwd workload %s" % w.name)
     inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed, spiky_keys=w.spiky_keys)
     o, lse = run_fwd(inp, w.dtype, w.causal, w.scale)

@@ -36,7 +36,8 @@ def test_splitkv_small(B, H, N, splits, D, causal, dtype):
 
 
 @pytest.mark.parametrize("w,splits", [(workloads.SMALL, 4), (workloads.CAUSAL_D128[512], 4),
-                                      (workloads.CAUSAL_D128[1024], 2)], ids=["small_s4", "n512_s4", "n1024_s2"])
+                                      (workloads.CAUSAL_D128[1024], 2), (workloads.FEW_HEADS_LONG, 4)],
+                         ids=["small_s4", "n512_s4", "n1024_s2", "one_head_n16384_s4"])
 def test_splitkv_workload(w, splits):
     say("splitkv workload %s splits=%d" % (w.name, splits))
     inp = make_inputs(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed)
