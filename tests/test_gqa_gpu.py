@@ -78,6 +78,25 @@ def test_gqa_long_sampled_heads():
         assert_grads_close(got, ref, "group %d" % hk)
 
 
+def test_mqa_headline_shape_all_heads():
+    """One K/V head for the 32 query heads of the headline shape (causal
+    fp16 B1 N8192 D128), as the bench times it: O and LSE of every query
+    head, dQ of every head and the group-summed dK, dV against the oracle."""
+    B, H, Hkv, N, D = 1, 32, 1, 8192, 128
+    say("MQA B=%d H=%d H_kv=%d N=%d D=%d, all heads" % (B, H, Hkv, N, D))
+    inp = gqa_inputs(B, H, Hkv, N, D, "fp16", 6300)
+    q, k, v, do = (to_dev(inp[n], "fp16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(D)
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], True, scale)
+    assert_fwd_close(to_host(o), to_host(lse), o_ref, lse_ref, "fp16", "MQA, all %d heads" % H)
+    del o_ref, lse_ref
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], True, scale)
+    assert_grads_close([to_host(dq), to_host(dk), to_host(dv)], ref, "MQA, all %d heads" % H)
+
+
 def test_gqa_with_key_mask():
     B, H, Hkv, N, D = 2, 6, 2, 300, 64
     inp = gqa_inputs(B, H, Hkv, N, D, "bf16", 6300)
