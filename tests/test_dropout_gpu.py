@@ -113,24 +113,29 @@ def test_dropout_zero_probability_matches_plain_forward(D):
     assert_grads_close([to_host(t) for t in g1], ref, "p=0 D=%d" % D)
 
 
-def test_dropout_long_sampled_heads():
-    # the C5 geometry (causal fp16, H = 32, N = 4096, D = 64) with p = 0.1;
-    # a sampled head is checked alone with the counter's head number of the
-    # full problem (the oracle's head_numbers)
-    B, H, N, D = 1, 32, 4096, 64
-    inp = make_inputs(B, H, N, D, "fp16", seed=5, with_dout=True)
+@pytest.mark.parametrize("N,D,in_seed,heads", [(4096, 64, 5, (0, 17)), (8192, 128, 3, (0, 31))],
+                         ids=["n4096_d64", "n8192_d128"])
+def test_dropout_long_sampled_heads(N, D, in_seed, heads):
+    # the C5 geometry (causal fp16, H = 32, N = 4096, D = 64) and the headline
+    # one (N = 8192, D = 128) with p = 0.1; a sampled head is checked alone
+    # with the counter's head number of the full problem (the oracle's
+    # head_numbers)
+    B, H = 1, 32
+    say("dropout p=0.1 B=%d H=%d N=%d D=%d causal, heads %s" % (B, H, N, D, heads))
+    inp = make_inputs(B, H, N, D, "fp16", seed=in_seed, with_dout=True)
     q, k, v, do = (to_dev(inp[n], "fp16") for n in ("q", "k", "v", "do"))
     p, seed, offset = 0.1, 2024, 0
     o, lse = fa.fwd_dropout(q, k, v, p, seed, offset, causal=True)
     dq, dk, dv = fa.bwd_dropout(q, k, v, o, lse, do, p, seed, offset, causal=True)
     torch.cuda.synchronize()
-    for h in (0, 17):
+    scale = 1.0 / np.sqrt(D)
+    for h in heads:
         sl = (slice(0, 1), slice(h, h + 1))
         sub = [inp[n][sl] for n in ("q", "k", "v", "do")]
         drop = (p, seed, offset, [[h]])
-        o_ref, lse_ref = attention_forward(*sub[:3], True, 0.125, dropout=drop)
+        o_ref, lse_ref = attention_forward(*sub[:3], True, scale, dropout=drop)
         assert_fwd_close(to_host(o[sl]), to_host(lse[sl]), o_ref, lse_ref, "fp16", "head %d" % h)
-        grads = attention_backward(*sub, True, 0.125, dropout=drop)
+        grads = attention_backward(*sub, True, scale, dropout=drop)
         assert_grads_close([to_host(t[sl]) for t in (dq, dk, dv)], grads, "head %d" % h)
 
 
