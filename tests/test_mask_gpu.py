@@ -112,6 +112,30 @@ def test_fwd_masked_all_visible_is_bitwise_fwd(N, H, causal):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def test_masked_headline_shape_all_heads():
+    """The headline shape (causal fp16 B1 H32 N8192 D128) with the seeded
+    length mask the bench times (keys past a drawn length hidden): O, LSE
+    and all gradients of every head against the oracle."""
+    B, H, N, D = 1, 32, 8192, 128
+    m = make_key_mask(B, N, "lengths", seed=3, p=0.5)
+    say("masked headline shape, visible length %d, all heads" % int(m.sum()))
+    inp = make_inputs(B, H, N, D, "fp16", seed=3, with_dout=True)
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = (to_dev(inp[n], "fp16") for n in ("q", "k", "v", "do"))
+    tiles = fa.mask_tiles(torch.from_numpy(m).cuda())
+    o, lse = fa.fwd_masked(q, k, v, tiles, causal=True, scale=scale)
+    dq, dk, dv = fa.bwd_masked(q, k, v, o, lse, do, tiles, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_forward(inp["q"], inp["k"], inp["v"], True, scale, key_mask=m)
+    _assert_masked_fwd(o, lse, o_ref, lse_ref, "fp16", "all %d heads" % H)
+    del o_ref, lse_ref
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], True, scale, key_mask=m)
+    got = [to_host(t) for t in (dq, dk, dv)]
+    assert_grads_close(got, ref, "masked headline shape, all %d heads" % H)
+    hidden = m[0] == 0
+    assert np.all(got[1][0][:, hidden] == 0) and np.all(got[2][0][:, hidden] == 0)
+
+
 def test_fwd_masked_long_sequences_sampled_heads():
     # the C2 geometry (H=32, N=4096, D=64) split over a padded batch of 2
     B, H, N, D = 2, 16, 4096, 64
